@@ -1,0 +1,257 @@
+"""Benchmark of the fused residual + gate + LayerNorm + scale/shift path on one MI355X.
+
+Workload (one step = one launch of the fused op over the whole batch): WAN2.2
+T2V-A14B at 720p / 193 frames -- 49 latent frames x 3600 tokens = sequence
+176400, model width 5120, LayerNorm without affine, gated residual, with the
+4D per-frame gate / scale / shift layout (B=1, F=49): the shape of sglang
+PR #36349, "Microbenchmark", with synthetic N(0,1) activations.  Inputs are
+resident in HBM before the timed region.
+
+Metric: algorithmic HBM bytes (every operand read once + every output written
+once) / time, in GB/s (1e9 B/s), against the 8 TB/s HBM3E peak.  The
+norm-only companion (same shape, broadcast scale/shift) is reported beside it.
+
+Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
+GPU), --steps K, --warmup W, --calibrate (time a plain elementwise copy, used to
+scale rocprof byte counters), --no-cpu-baseline, --workload NAME.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+HEADLINE = "fused_ln_frame_b1_f49_l176400_d5120"
+COMPANION = "nss_ln_b1_l176400_d5120"
+KERNEL_SOURCES = ["rmsnorm_diffusion_transformers_amd/csrc/rn_row_kernel.hpp",
+                  "rmsnorm_diffusion_transformers_amd/csrc/rn_args.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprof counters, if they were taken
+    on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = t.get("workloads", {}).get(workload)
+    if not rec or rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def upload(inp, dev):
+    import numpy as np
+    import torch
+    return {k: torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+            for k, v in inp.items()}
+
+
+def time_workload(rn, wl, steps, warmup, dev):
+    import torch
+
+    import synth
+
+    t0 = time.time()
+    inp = synth.make_inputs(wl, threads=threads())
+    log("%s: inputs generated in %.1f s" % (wl.name, time.time() - t0))
+    d = upload(inp, dev)
+    del inp
+    y = torch.empty_like(d["x"])
+    ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        launch_workload(rn, wl, d, y, ro, stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        launch_workload(rn, wl, d, y, ro, stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = start.elapsed_time(end) / steps
+    del d, y, ro
+    torch.cuda.empty_cache()
+    return ms, wall
+
+
+def launch_workload(rn, wl, d, y, ro, stream):
+    """One pass of the workload through the C entry points."""
+    flags = (rn.RN_RMS if wl.is_rms else 0) | (rn.RN_WEIGHT if wl.has_weight else 0) | \
+        (rn.RN_BIAS if wl.has_bias else 0)
+    if wl.op == "fused":
+        if wl.gate_layout is not None:
+            flags |= rn.RN_GATE
+        rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d.get("gate"), d.get("weight"),
+                             d.get("bias"), d["scale"], d["shift"], wl.B, wl.L, wl.D, flags,
+                             wl.gate_layout or (0, 0), wl.ss_layout, wl.eps, stream)
+    else:
+        rn.norm_scale_shift_fwd(y, d["x"], d.get("weight"), d.get("bias"), d["scale"],
+                                d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps, stream)
+
+
+def calibrate(steps, warmup, dev):
+    """A plain elementwise copy (torch.neg on bf16: reads N bytes, writes N
+    bytes) on a tensor of the headline's activation size."""
+    import torch
+    n = 176400 * 5120
+    x = torch.randn(n, device=dev).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        torch.neg(x, out=y)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    out = {"metric": "elementwise copy (calibration)", "bytes_read": 2 * n, "bytes_written": 2 * n,
+           "ms": ms, "GB/s": 4 * n / ms / 1e6}
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl):
+    """The oracle (as it is) on a bounded sample of the same workload, on this
+    host's cores.  Returns the record for the JSON line."""
+    import synth
+    import oracle
+    rows = 32768
+    n = threads()
+    rows = min(rows, wl.R)
+    t0 = time.time()
+    inp = _first_rows(wl, rows, n)
+    log("cpu baseline: inputs for %d rows in %.1f s" % (rows, time.time() - t0))
+    o = oracle.Oracle()
+    t0 = time.perf_counter()
+    o.run_workload(wl, inp, row0=0, nrows=rows, threads=n)
+    dt = time.perf_counter() - t0
+    per_row = wl.algorithmic_bytes() / wl.R
+    return {"value": round(rows * per_row / dt / 1e9, 3), "unit": "GB/s", "cores": n,
+            "kind": "oracle", "rows_per_s": round(rows / dt, 1),
+            "sample": "first %d of %d rows of %s (all operands they read), oracle threads=%d, "
+                      "%.2f s wall" % (rows, wl.R, wl.name, n, dt)}
+
+
+def _first_rows(wl, rows, n):
+    """Inputs of the first `rows` activation rows (modulation tensors whole)."""
+    import synth
+    d = wl.dists
+    out = {"x": synth.fill(d[synth.X], wl.wid, rows * wl.D, row_len=wl.D, stress=wl.stress,
+                           threads=n).reshape(rows, wl.D)}
+    if wl.op == "fused":
+        out["residual"] = synth.fill(d[synth.RES], wl.wid, rows * wl.D, row_len=wl.D,
+                                     stress=wl.stress, threads=n).reshape(rows, wl.D)
+        if wl.gate_layout is not None:
+            g = wl.mod_rows(wl.gate_layout)
+            out["gate"] = synth.fill(d[synth.GATE], wl.wid, g * wl.D, threads=n).reshape(g, wl.D)
+    m = wl.mod_rows(wl.ss_layout)
+    out["scale"] = synth.fill(d[synth.SCALE], wl.wid, m * wl.D, threads=n).reshape(m, wl.D)
+    out["shift"] = synth.fill(d[synth.SHIFT], wl.wid, m * wl.D, threads=n).reshape(m, wl.D)
+    if wl.has_weight:
+        out["weight"] = synth.fill(d[synth.WEIGHT], wl.wid, wl.D, threads=n)
+    if wl.has_bias:
+        out["bias"] = synth.fill(d[synth.BIAS], wl.wid, wl.D, threads=n)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-companion", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures this path on exactly one GPU (the row-wise op needs no "
+              "communication; see the sharding note in the design document); --gpus %d is "
+              "not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if args.calibrate:
+        calibrate(args.steps, args.warmup, dev)
+        return
+
+    import rmsnorm_diffusion_transformers_amd as rn
+    import synth
+    wl = synth.WORKLOADS[args.workload]
+    ms, wall = time_workload(rn, wl, args.steps, args.warmup, dev)
+    nbytes = wl.algorithmic_bytes()
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log("%s: %.4f ms/launch, %.1f GB/s (%.1f%% of %g)" % (wl.name, ms, gbs, 100 * gbs / HBM_PEAK_GBS,
+                                                          HBM_PEAK_GBS))
+    companions = []
+    if not args.no_companion and args.workload == HEADLINE:
+        wc = synth.WORKLOADS[COMPANION]
+        cms, _ = time_workload(rn, wc, args.steps, args.warmup, dev)
+        cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
+        log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
+        companions.append({"workload": wc.name, "ms_per_launch": round(cms, 5),
+                           "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": wc.algorithmic_bytes(),
+                           "traffic": measured_traffic(wc.name)})
+    info = rn.describe_launch(wl.B, wl.L, wl.D, 0, wl.op == "fused")
+    line = {
+        "metric": "fused residual-norm HBM GB/s and % of peak, bf16 L=176400 D=5120",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, U(0,1) gate, N(0,0.1) scale/shift)",
+        "config": {"workload": wl.name, "op": wl.op, "norm": "rms" if wl.is_rms else "layer",
+                   "B": wl.B, "L": wl.L, "D": wl.D, "frames": 49 if wl.gate_layout == (2, 49) else None,
+                   "gate_layout": wl.gate_layout, "ss_layout": wl.ss_layout,
+                   "algorithmic_bytes": nbytes, "launch": info},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)},
+        "wall_s_timed_region": round(wall, 4),
+        "companions": companions,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

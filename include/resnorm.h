@@ -1,0 +1,143 @@
+/*
+ * resnorm.h -- C ABI of the MI355X (gfx950) fused residual-norm library.
+ *
+ * The row-wise hot path of a video diffusion transformer block: a gated
+ * residual update followed by LayerNorm or RMSNorm and the adaLN-style
+ * scale/shift modulation, on [B, L, D] bf16 activations.  The two operations
+ * are those of the custom ops flydsl_fused_residual_norm_scale_shift and
+ * flydsl_norm_scale_shift, with the same operand order (sglang PR #36349,
+ * "[AMD][Diffusion] Migrate FlyDSL fused norm kernels to the v0.3.0 stable
+ * API", section "Microbenchmark", reproduction snippet), and the
+ * specialisation matrix is_rms x has_gate x has_weight plus the broadcast,
+ * per-row and 4D per-frame modulation layouts (sglang PR #33144, same title,
+ * sections "Modifications" and "Accuracy Tests").
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers to bf16 data (raw bits), owned
+ *     by the caller, contiguous row-major, 16-byte aligned.  Row stride = D.
+ *   - The library never allocates, frees or synchronises.  Work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the null stream) and the call returns;
+ *     the outputs are valid once the stream reaches that point.
+ *   - Activation row r = b * L + l (batch b, token l), 0 <= r < B * L.
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     non-OK status nothing was enqueued and rn_last_error() describes the
+ *     problem.  There is no fallback path: an unsupported case is an error.
+ *   - B * L == 0 is valid and enqueues nothing.
+ *   - Exact aliasing y == x and residual_out == residual is allowed (each
+ *     element is read before it is overwritten, by the same thread); any other
+ *     overlap between an output and another operand is RN_EINVAL.
+ *   - The library is thread-safe; calls that overlap in time and write the
+ *     same memory race, as any two kernels would.
+ */
+#ifndef RESNORM_H
+#define RESNORM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RN_OK = 0,
+  RN_EINVAL = 1,        /* invalid argument (null/misaligned pointer, bad shape, flag/pointer mismatch, overlap) */
+  RN_EUNSUPPORTED = 2,  /* valid but outside what the kernels support (D > RN_D_MAX, B*L >= 2^31) */
+  RN_ELAUNCH = 3        /* the HIP runtime refused the launch (see rn_last_error) */
+} rn_status;
+
+/* Bits of `flags`. */
+enum {
+  RN_RMS = 1u << 0,     /* RMSNorm (no centring) instead of LayerNorm */
+  RN_GATE = 1u << 1,    /* residual_out = residual + gate * x (else residual + x); fused op only */
+  RN_WEIGHT = 1u << 2,  /* multiply the normalised row by weight[D] */
+  RN_BIAS = 1u << 3     /* then add bias[D]; requires RN_WEIGHT */
+};
+
+/* How an activation row selects its row of a modulation operand (gate, or
+ * scale and shift, which share one layout). */
+typedef enum {
+  RN_BCAST = 0,  /* one dense (1, D) row shared by every activation row (every batch too) */
+  RN_ROW = 1,    /* a (B, L, D) tensor: row r */
+  RN_FRAME = 2   /* a (B, F, 1, D) tensor, tokens frame-major: row b*F + l / (L/F); needs L % F == 0 */
+} rn_layout_kind;
+
+typedef struct {
+  int32_t kind;    /* rn_layout_kind */
+  int32_t frames;  /* F for RN_FRAME (>= 1); ignored otherwise */
+} rn_layout;
+
+/* Largest supported row width. */
+#define RN_D_MAX 16384
+
+/*
+ * resnorm_fused_fwd -- gated residual update + norm + modulation.
+ *
+ * For every activation row r and column c (sglang PR #36349, "Microbenchmark":
+ * flydsl_fused_residual_norm_scale_shift(residual, x, gate, weight, bias,
+ * scale, shift, norm_type, eps); the formula is this library's reading of it):
+ *   s                   = f32(residual[r,c]) + f32(gate[g(r),c]) * f32(x[r,c])   (binary32)
+ *   residual_out[r,c]   = bf16_rne(s)
+ *   h                   = residual_out[r, :] as f32
+ *   LayerNorm:  n = (h - mean(h)) * rsqrt(var(h) + eps)    (biased variance, 1/D)
+ *   RMSNorm:    n = h * rsqrt(mean(h^2) + eps)
+ *   n = n * weight[c] (+ bias[c])                            (if RN_WEIGHT / RN_BIAS)
+ *   y[r,c]             = bf16_rne(n * (1 + scale[s(r),c]) + shift[s(r),c])
+ * g(r), s(r) are the rows selected by gate_layout and ss_layout.
+ *
+ *   y, residual_out  [B*L, D] outputs (y may be x; residual_out may be residual)
+ *   x, residual      [B*L, D] inputs
+ *   gate             rows per gate_layout; must be NULL iff !(flags & RN_GATE)
+ *   weight, bias     [D]; NULL iff the corresponding flag is clear
+ *   scale, shift     rows per ss_layout; required
+ *   B, L, D          B, L >= 0; 8 <= D <= RN_D_MAX, D % 8 == 0
+ *   flags            RN_RMS | RN_GATE | RN_WEIGHT | RN_BIAS
+ *   eps              finite, >= 0 (added inside the square root)
+ *   stream           hipStream_t to enqueue on
+ * Returns RN_OK once enqueued, else an error status (nothing enqueued).
+ */
+rn_status resnorm_fused_fwd(void* y, void* residual_out, const void* x, const void* residual,
+                            const void* gate, const void* weight, const void* bias,
+                            const void* scale, const void* shift, int64_t B, int64_t L,
+                            int64_t D, uint32_t flags, rn_layout gate_layout,
+                            rn_layout ss_layout, float eps, void* stream);
+
+/*
+ * norm_scale_shift_fwd -- norm + modulation without residual or gate
+ * (flydsl_norm_scale_shift(x, weight, bias, scale, shift, norm_type, eps),
+ * sglang PR #36349, "Microbenchmark"): the formula above with h = x.
+ *
+ *   y       [B*L, D] output (may be x)
+ *   x       [B*L, D] input
+ *   weight, bias, scale, shift, B, L, D, eps, stream: as above
+ *   flags   RN_RMS | RN_WEIGHT | RN_BIAS (RN_GATE is RN_EINVAL)
+ */
+rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const void* bias,
+                               const void* scale, const void* shift, int64_t B, int64_t L,
+                               int64_t D, uint32_t flags, rn_layout ss_layout, float eps,
+                               void* stream);
+
+/* Text describing the last non-OK status returned on the calling thread
+ * (empty if none).  The pointer stays valid until the thread's next call. */
+const char* rn_last_error(void);
+
+/* Launch shape the library would use for a problem (host-only query; no
+ * device work, usable without a GPU): vectors of 8 bf16 per lane, waves per
+ * workgroup, rows per workgroup, workgroup size and grid size. */
+typedef struct {
+  int32_t vec_per_lane;
+  int32_t waves_per_block;
+  int32_t rows_per_block;
+  int32_t block_threads;
+  int64_t grid_blocks;
+} rn_launch_info;
+
+rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
+                             rn_launch_info* info);
+
+/* Library version string. */
+const char* rn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RESNORM_H */

@@ -1,0 +1,226 @@
+"""Fused residual + gate + LayerNorm/RMSNorm + scale/shift for video diffusion
+transformers on MI355X (gfx950).
+
+A thin ctypes binding over ``librnorm.so`` (C ABI in ``include/resnorm.h``).
+It only marshals arguments: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback: if the library is not built,
+importing this package raises ImportError; if a call is rejected, it raises
+``RnError`` with the library's message.
+
+Low level (same names and argument order as the C entry points):
+    resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale,
+                      shift, B, L, D, flags, gate_layout, ss_layout, eps, stream)
+    norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
+                         ss_layout, eps, stream)
+Tensor level (operand order of the custom ops flydsl_fused_residual_norm_scale_shift
+and flydsl_norm_scale_shift, sglang PR #36349, "Microbenchmark"):
+    fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
+                                    norm_type, eps) -> (y, residual_out)
+    norm_scale_shift(x, weight, bias, scale, shift, norm_type, eps) -> y
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librnorm.so")
+
+RN_OK, RN_EINVAL, RN_EUNSUPPORTED, RN_ELAUNCH = 0, 1, 2, 3
+RN_RMS, RN_GATE, RN_WEIGHT, RN_BIAS = 1, 2, 4, 8
+RN_BCAST, RN_ROW, RN_FRAME = 0, 1, 2
+RN_D_MAX = 16384
+_STATUS = {0: "RN_OK", 1: "RN_EINVAL", 2: "RN_EUNSUPPORTED", 3: "RN_ELAUNCH"}
+
+
+class rn_layout(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("frames", ctypes.c_int32)]
+
+
+class rn_launch_info(ctypes.Structure):
+    _fields_ = [("vec_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int64)]
+
+
+class RnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("librnorm.so is not built (expected at %s); build it with "
+                          "__graft_entry__.build() or python %s/_build.py" % (LIB_PATH, _HERE))
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, U32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+    lib.resnorm_fused_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, U32,
+                                      rn_layout, rn_layout, F32, P]
+    lib.resnorm_fused_fwd.restype = ctypes.c_int
+    lib.norm_scale_shift_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, U32, rn_layout, F32, P]
+    lib.norm_scale_shift_fwd.restype = ctypes.c_int
+    lib.rn_last_error.argtypes = []
+    lib.rn_last_error.restype = ctypes.c_char_p
+    lib.rn_describe_launch.argtypes = [I64, I64, I64, U32, ctypes.c_int32,
+                                       ctypes.POINTER(rn_launch_info)]
+    lib.rn_describe_launch.restype = ctypes.c_int
+    lib.rn_version.argtypes = []
+    lib.rn_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def last_error() -> str:
+    return _lib.rn_last_error().decode()
+
+
+def version() -> str:
+    return _lib.rn_version().decode()
+
+
+def _check(status: int):
+    if status != RN_OK:
+        raise RnError(status, last_error())
+
+
+def _addr(t):
+    """Device address of a bf16 CUDA tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor, an int address or None, got %r" % type(t))
+    if t.device.type != "cuda":
+        raise ValueError("tensor must be on a GPU device (got %s); there is no CPU path" % t.device)
+    if t.dtype != torch.bfloat16:
+        raise TypeError("tensor must be bfloat16 (got %s)" % t.dtype)
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _layout(lay) -> rn_layout:
+    if isinstance(lay, rn_layout):
+        return lay
+    kind, frames = lay
+    return rn_layout(int(kind), int(frames))
+
+
+def resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                      flags, gate_layout=(RN_BCAST, 0), ss_layout=(RN_BCAST, 0), eps=1e-6,
+                      stream=None) -> None:
+    """Enqueue the fused op (C entry point of the same name); raises RnError."""
+    _check(_lib.resnorm_fused_fwd(_addr(y), _addr(residual_out), _addr(x), _addr(residual),
+                                  _addr(gate), _addr(weight), _addr(bias), _addr(scale),
+                                  _addr(shift), int(B), int(L), int(D), int(flags),
+                                  _layout(gate_layout), _layout(ss_layout), float(eps),
+                                  _stream(stream)))
+
+
+def norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
+                         ss_layout=(RN_BCAST, 0), eps=1e-6, stream=None) -> None:
+    """Enqueue the norm-only op (C entry point of the same name); raises RnError."""
+    _check(_lib.norm_scale_shift_fwd(_addr(y), _addr(x), _addr(weight), _addr(bias),
+                                     _addr(scale), _addr(shift), int(B), int(L), int(D),
+                                     int(flags), _layout(ss_layout), float(eps),
+                                     _stream(stream)))
+
+
+def describe_launch(B, L, D, flags, fused=True) -> dict:
+    info = rn_launch_info()
+    _check(_lib.rn_describe_launch(int(B), int(L), int(D), int(flags), int(bool(fused)),
+                                   ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in rn_launch_info._fields_}
+
+
+def infer_layout(t, B: int, L: int, D: int) -> tuple:
+    """Modulation layout from a tensor's shape, relative to activations [B, L, D]:
+    (D,), (1, D), (1, 1, D) -> broadcast; (B, L, D) -> per row; (B, F, 1, D) ->
+    per frame with F frames; (B, D) and (B, 1, D) -> per batch (per frame, F = 1)."""
+    s = tuple(t.shape)
+    if s in ((D,), (1, D), (1, 1, D), (1, 1, 1, D)):
+        return (RN_BCAST, 0)
+    if s == (B, L, D):
+        return (RN_ROW, 0)
+    if len(s) == 4 and s[0] == B and s[2] == 1 and s[3] == D and s[1] >= 1:
+        return (RN_FRAME, s[1])
+    if s in ((B, D), (B, 1, D)):
+        return (RN_FRAME, 1)
+    raise ValueError("cannot map modulation shape %s onto activations (%d, %d, %d)" % (s, B, L, D))
+
+
+def _norm_flag(norm_type: str) -> int:
+    if norm_type == "layer":
+        return 0
+    if norm_type == "rms":
+        return RN_RMS
+    raise ValueError("norm_type must be 'layer' or 'rms' (got %r)" % (norm_type,))
+
+
+def _bld(x):
+    if x.dim() == 3:
+        return x.shape
+    if x.dim() == 2:
+        return (1, x.shape[0], x.shape[1])
+    raise ValueError("activations must be [B, L, D] or [L, D] (got %s)" % (tuple(x.shape),))
+
+
+def fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
+                                    norm_type: str = "layer", eps: float = 1e-6, *, y=None,
+                                    residual_out=None, stream=None):
+    """residual_out = residual + gate * x; y = norm(residual_out) [* weight + bias]
+    * (1 + scale) + shift.  Returns (y, residual_out), both bf16 like x."""
+    import torch
+    B, L, D = _bld(x)
+    flags = _norm_flag(norm_type)
+    if gate is not None:
+        flags |= RN_GATE
+    if weight is not None:
+        flags |= RN_WEIGHT
+    if bias is not None:
+        flags |= RN_BIAS
+    if y is None:
+        y = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(residual)
+    gl = infer_layout(gate, B, L, D) if gate is not None else (RN_BCAST, 0)
+    sl = infer_layout(scale, B, L, D)
+    if infer_layout(shift, B, L, D) != sl:
+        raise ValueError("scale and shift must share one layout")
+    resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                      flags, gl, sl, eps, stream)
+    return y, residual_out
+
+
+def norm_scale_shift(x, weight, bias, scale, shift, norm_type: str = "layer", eps: float = 1e-6,
+                     *, y=None, stream=None):
+    """y = norm(x) [* weight + bias] * (1 + scale) + shift (bf16 like x)."""
+    import torch
+    B, L, D = _bld(x)
+    flags = _norm_flag(norm_type)
+    if weight is not None:
+        flags |= RN_WEIGHT
+    if bias is not None:
+        flags |= RN_BIAS
+    if y is None:
+        y = torch.empty_like(x)
+    sl = infer_layout(scale, B, L, D)
+    if infer_layout(shift, B, L, D) != sl:
+        raise ValueError("scale and shift must share one layout")
+    norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags, sl, eps, stream)
+    return y

@@ -1,0 +1,267 @@
+// rn_api.hip -- the C ABI declared in include/resnorm.h: argument validation,
+// launch planning and the enqueue of the gfx950 row kernels.
+//
+// Host-side rules (all checked before anything is enqueued):
+//   * operand presence must match the flags (a present-but-unflagged operand
+//     is an error, as is a flagged-but-missing one), so a caller cannot
+//     silently get a different specialisation than it asked for;
+//   * D % 8 == 0 (16-byte vectors), 8 <= D <= RN_D_MAX, every pointer 16-byte
+//     aligned, B * L < 2^31 (32-bit row indices in the kernels);
+//   * a per-frame layout needs 1 <= F and L % F == 0 (frame-major tokens:
+//     49 frames x 3600 tokens in sglang PR #36349, "Microbenchmark");
+//   * eps is honoured and must be finite and >= 0 (the prior-art kernel
+//     ignored it and hard-coded 1e-6: sglang PR #33144, "Modifications");
+//   * an empty problem (B * L == 0) returns OK without a launch (the prior art
+//     had no empty-tensor guard: sglang PR #33144, "Known gaps").
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cmath>
+
+#include "../../include/resnorm.h"
+#include "rn_args.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+rn_status fail(rn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+struct Extent {
+  const char* name;
+  uintptr_t lo;
+  uintptr_t hi;  // one past the end
+  bool output;
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t layout_rows(rn_layout lay, int64_t B, int64_t L) {
+  switch (lay.kind) {
+    case RN_BCAST: return 1;
+    case RN_ROW: return B * L;
+    case RN_FRAME: return B * (int64_t)lay.frames;
+    default: return -1;
+  }
+}
+
+rn_status check_layout(const char* what, rn_layout lay, int64_t L) {
+  if (lay.kind != RN_BCAST && lay.kind != RN_ROW && lay.kind != RN_FRAME)
+    return fail(RN_EINVAL, "%s layout kind %d is not RN_BCAST, RN_ROW or RN_FRAME", what, (int)lay.kind);
+  if (lay.kind == RN_FRAME) {
+    if (lay.frames < 1) return fail(RN_EINVAL, "%s layout RN_FRAME needs frames >= 1 (got %d)", what, (int)lay.frames);
+    if (L % lay.frames != 0)
+      return fail(RN_EINVAL, "%s layout RN_FRAME needs L %% frames == 0 (L=%lld, frames=%d)", what,
+                  (long long)L, (int)lay.frames);
+  }
+  return RN_OK;
+}
+
+struct Problem {
+  bool fused;
+  void* y;
+  void* residual_out;
+  const void* x;
+  const void* residual;
+  const void* gate;
+  const void* weight;
+  const void* bias;
+  const void* scale;
+  const void* shift;
+  int64_t B, L, D;
+  uint32_t flags;
+  rn_layout gate_layout, ss_layout;
+  float eps;
+};
+
+rn_status check_shape(int64_t B, int64_t L, int64_t D, uint32_t flags, bool fused) {
+  const uint32_t known = RN_RMS | RN_GATE | RN_WEIGHT | RN_BIAS;
+  if (flags & ~known) return fail(RN_EINVAL, "unknown flag bits 0x%x", flags & ~known);
+  if (!fused && (flags & RN_GATE)) return fail(RN_EINVAL, "RN_GATE is only valid for resnorm_fused_fwd");
+  if ((flags & RN_BIAS) && !(flags & RN_WEIGHT)) return fail(RN_EINVAL, "RN_BIAS requires RN_WEIGHT");
+  if (B < 0 || L < 0) return fail(RN_EINVAL, "negative shape (B=%lld, L=%lld)", (long long)B, (long long)L);
+  if (D < 8 || D % 8 != 0) return fail(RN_EINVAL, "D must be a positive multiple of 8 (got %lld)", (long long)D);
+  if (D > RN_D_MAX) return fail(RN_EUNSUPPORTED, "D=%lld exceeds RN_D_MAX=%d", (long long)D, RN_D_MAX);
+  if (L > 0 && B > ((int64_t)1 << 31) / L) return fail(RN_EUNSUPPORTED, "B*L >= 2^31 rows is not supported");
+  if (B * L >= ((int64_t)1 << 31)) return fail(RN_EUNSUPPORTED, "B*L >= 2^31 rows is not supported");
+  return RN_OK;
+}
+
+int vec_index_for(int64_t D) {
+  const int64_t need = (D / 8 + rn::kWaveSize - 1) / rn::kWaveSize;
+  for (int i = 0; i < rn::kNumVecWidths; ++i)
+    if (rn::kVecWidths[i] >= need) return i;
+  return -1;
+}
+
+rn_status validate(const Problem& p) {
+  rn_status st = check_shape(p.B, p.L, p.D, p.flags, p.fused);
+  if (st != RN_OK) return st;
+  const bool want_gate = p.flags & RN_GATE, want_w = p.flags & RN_WEIGHT, want_b = p.flags & RN_BIAS;
+
+  if (!p.y) return fail(RN_EINVAL, "y is NULL");
+  if (!p.x) return fail(RN_EINVAL, "x is NULL");
+  if (!p.scale) return fail(RN_EINVAL, "scale is NULL");
+  if (!p.shift) return fail(RN_EINVAL, "shift is NULL");
+  if (p.fused) {
+    if (!p.residual) return fail(RN_EINVAL, "residual is NULL");
+    if (!p.residual_out) return fail(RN_EINVAL, "residual_out is NULL");
+    if (want_gate != (p.gate != nullptr))
+      return fail(RN_EINVAL, want_gate ? "RN_GATE set but gate is NULL" : "gate given but RN_GATE not set");
+  }
+  if (want_w != (p.weight != nullptr))
+    return fail(RN_EINVAL, want_w ? "RN_WEIGHT set but weight is NULL" : "weight given but RN_WEIGHT not set");
+  if (want_b != (p.bias != nullptr))
+    return fail(RN_EINVAL, want_b ? "RN_BIAS set but bias is NULL" : "bias given but RN_BIAS not set");
+  if (!std::isfinite(p.eps) || p.eps < 0.f) return fail(RN_EINVAL, "eps must be finite and >= 0 (got %g)", (double)p.eps);
+
+  if (p.fused && want_gate && (st = check_layout("gate", p.gate_layout, p.L)) != RN_OK) return st;
+  if ((st = check_layout("scale/shift", p.ss_layout, p.L)) != RN_OK) return st;
+
+  const void* ptrs[] = {p.y, p.residual_out, p.x, p.residual, p.gate, p.weight, p.bias, p.scale, p.shift};
+  const char* names[] = {"y", "residual_out", "x", "residual", "gate", "weight", "bias", "scale", "shift"};
+  for (int i = 0; i < 9; ++i)
+    if (ptrs[i] && !aligned16(ptrs[i])) return fail(RN_EINVAL, "%s is not 16-byte aligned", names[i]);
+
+  // Overlap: outputs against every other operand; only exact y == x and
+  // residual_out == residual are allowed.
+  const int64_t R = p.B * p.L;
+  const uint64_t row = (uint64_t)p.D * 2u;
+  Extent ext[9];
+  int n = 0;
+  auto add = [&](const char* name, const void* ptr, int64_t rows, bool output) {
+    if (ptr && rows > 0)
+      ext[n++] = Extent{name, (uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)(rows * row), output};
+  };
+  add("y", p.y, R, true);
+  if (p.fused) add("residual_out", p.residual_out, R, true);
+  add("x", p.x, R, false);
+  if (p.fused) add("residual", p.residual, R, false);
+  if (p.fused && want_gate) add("gate", p.gate, layout_rows(p.gate_layout, p.B, p.L), false);
+  add("weight", p.weight, 1, false);
+  add("bias", p.bias, 1, false);
+  add("scale", p.scale, layout_rows(p.ss_layout, p.B, p.L), false);
+  add("shift", p.shift, layout_rows(p.ss_layout, p.B, p.L), false);
+  // Inputs may share memory with each other (they are only read).
+  for (int i = 0; i < n; ++i) {
+    if (!ext[i].output) continue;
+    for (int j = 0; j < n; ++j) {
+      if (i == j) continue;
+      const Extent& a = ext[i];
+      const Extent& b = ext[j];
+      if (a.lo >= b.hi || b.lo >= a.hi) continue;
+      const bool exact = a.lo == b.lo && a.hi == b.hi;
+      const bool allowed = exact && ((!strcmp(a.name, "y") && !strcmp(b.name, "x")) ||
+                                     (!strcmp(a.name, "residual_out") && !strcmp(b.name, "residual")));
+      if (!allowed) return fail(RN_EINVAL, "%s overlaps %s", a.name, b.name);
+    }
+  }
+  return RN_OK;
+}
+
+rn::KernelFn pick_kernel(const Problem& p, int vi) {
+  const int aff = (p.flags & RN_BIAS) ? rn::kAffWeightBias : (p.flags & RN_WEIGHT) ? rn::kAffWeight : rn::kAffNone;
+  const bool rms = p.flags & RN_RMS;
+  if (p.fused) {
+    const bool gate = p.flags & RN_GATE;
+    return rms ? rn::fused_rms_kernel(gate, aff, vi) : rn::fused_ln_kernel(gate, aff, vi);
+  }
+  return rms ? rn::nss_rms_kernel(aff, vi) : rn::nss_ln_kernel(aff, vi);
+}
+
+uint32_t tokens_per_frame(rn_layout lay, int64_t L) {
+  return lay.kind == RN_FRAME ? (uint32_t)(L / lay.frames) : 1u;
+}
+
+rn_status run(const Problem& p, void* stream) {
+  g_err[0] = '\0';
+  rn_status st = validate(p);
+  if (st != RN_OK) return st;
+  const int64_t R = p.B * p.L;
+  if (R == 0) return RN_OK;
+  const int vi = vec_index_for(p.D);
+  rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
+  if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
+
+  rn::RowArgs a;
+  a.x = p.x;
+  a.residual = p.residual;
+  a.gate = p.gate;
+  a.weight = p.weight;
+  a.bias = p.bias;
+  a.scale = p.scale;
+  a.shift = p.shift;
+  a.y = p.y;
+  a.residual_out = p.residual_out;
+  a.rows = (uint32_t)R;
+  a.L = (uint32_t)p.L;
+  a.d = (uint32_t)p.D;
+  a.nvec = (uint32_t)(p.D / 8);
+  a.eps = p.eps;
+  a.gate_kind = p.gate_layout.kind;
+  a.gate_frames = (uint32_t)(p.gate_layout.kind == RN_FRAME ? p.gate_layout.frames : 0);
+  a.gate_tokens_per_frame = tokens_per_frame(p.gate_layout, p.L);
+  a.ss_kind = p.ss_layout.kind;
+  a.ss_frames = (uint32_t)(p.ss_layout.kind == RN_FRAME ? p.ss_layout.frames : 0);
+  a.ss_tokens_per_frame = tokens_per_frame(p.ss_layout, p.L);
+  if (!(p.flags & RN_GATE)) a.gate_kind = RN_BCAST;
+
+  const int64_t blocks = (R + rn::kWavesPerBlock - 1) / rn::kWavesPerBlock;
+  void* args[] = {&a};
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)blocks), dim3(rn::kBlockThreads), args, 0,
+                                 (hipStream_t)stream);
+  if (e != hipSuccess) return fail(RN_ELAUNCH, "hipLaunchKernel failed: %s", hipGetErrorString(e));
+  return RN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rn_status resnorm_fused_fwd(void* y, void* residual_out, const void* x, const void* residual,
+                            const void* gate, const void* weight, const void* bias, const void* scale,
+                            const void* shift, int64_t B, int64_t L, int64_t D, uint32_t flags,
+                            rn_layout gate_layout, rn_layout ss_layout, float eps, void* stream) {
+  Problem p{true, y, residual_out, x, residual, gate, weight, bias, scale, shift,
+            B, L, D, flags, gate_layout, ss_layout, eps};
+  return run(p, stream);
+}
+
+rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const void* bias,
+                               const void* scale, const void* shift, int64_t B, int64_t L, int64_t D,
+                               uint32_t flags, rn_layout ss_layout, float eps, void* stream) {
+  Problem p{false, y, nullptr, x, nullptr, nullptr, weight, bias, scale, shift,
+            B, L, D, flags, rn_layout{RN_BCAST, 0}, ss_layout, eps};
+  return run(p, stream);
+}
+
+const char* rn_last_error(void) { return g_err; }
+
+rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
+                             rn_launch_info* info) {
+  g_err[0] = '\0';
+  if (!info) return fail(RN_EINVAL, "info is NULL");
+  rn_status st = check_shape(B, L, D, flags, fused != 0);
+  if (st != RN_OK) return st;
+  const int vi = vec_index_for(D);
+  if (vi < 0) return fail(RN_EUNSUPPORTED, "no register-cache width covers D=%lld", (long long)D);
+  info->vec_per_lane = rn::kVecWidths[vi];
+  info->waves_per_block = rn::kWavesPerBlock;
+  info->rows_per_block = rn::kWavesPerBlock;
+  info->block_threads = rn::kBlockThreads;
+  info->grid_blocks = (B * L + rn::kWavesPerBlock - 1) / rn::kWavesPerBlock;
+  return RN_OK;
+}
+
+const char* rn_version(void) { return "resnorm 0.1.0 gfx950"; }
+
+}  // extern "C"

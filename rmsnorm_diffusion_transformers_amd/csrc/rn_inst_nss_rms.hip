@@ -1,0 +1,13 @@
+// Compiled specialisations: nss rms (every affine / register-cache width).
+#include "rn_row_kernel.hpp"
+
+namespace rn {
+
+KernelFn nss_rms_kernel(int aff, int vec_index) {
+  if (aff == kAffNone) return kernel_for_width<true, false, false, kAffNone>(vec_index);
+  if (aff == kAffWeight) return kernel_for_width<true, false, false, kAffWeight>(vec_index);
+  if (aff == kAffWeightBias) return kernel_for_width<true, false, false, kAffWeightBias>(vec_index);
+  return nullptr;
+}
+
+}  // namespace rn

@@ -1,0 +1,74 @@
+"""Helpers for the GPU parity tests: device transfer of bf16 bit arrays, running
+a workload through the C ABI, and the oracle comparison at the contract's bar
+(residual_out bit-exact; y within max(2 ulp, 1e-2))."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+from util import check_y, ulp_diff
+
+
+def log(*a):
+    print("[gpu-test %s]" % time.strftime("%H:%M:%S"), *a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need an MI355X; torch.cuda.is_available() is False")
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dev=None):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    return t.to(dev or "cuda:0")
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def workload_flags(rn, wl) -> int:
+    f = rn.RN_RMS if wl.is_rms else 0
+    if wl.op == "fused" and wl.gate_layout is not None:
+        f |= rn.RN_GATE
+    if wl.has_weight:
+        f |= rn.RN_WEIGHT
+    if wl.has_bias:
+        f |= rn.RN_BIAS
+    return f
+
+
+def launch_workload(rn, wl, d: dict, y, ro=None, stream=None):
+    """Enqueue one pass of the workload on device tensors d -> y (and ro)."""
+    flags = workload_flags(rn, wl)
+    if wl.op == "fused":
+        rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d.get("gate"), d.get("weight"),
+                             d.get("bias"), d["scale"], d["shift"], wl.B, wl.L, wl.D, flags,
+                             wl.gate_layout or (0, 0), wl.ss_layout, wl.eps, stream)
+    else:
+        rn.norm_scale_shift_fwd(y, d["x"], d.get("weight"), d.get("bias"), d["scale"],
+                                d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps, stream)
+
+
+def compare_outputs(y_gpu, y_ref, ro_gpu=None, ro_ref=None, what=""):
+    """Assert the contract; return (max ulp error of y, fraction of y bit-identical)."""
+    if ro_ref is not None:
+        diff = np.flatnonzero(ro_gpu.ravel() != ro_ref.ravel())
+        assert diff.size == 0, "%s residual_out differs at %d elements (first flat index %d: gpu %04x oracle %04x)" % (
+            what, diff.size, diff[0], ro_gpu.ravel()[diff[0]], ro_ref.ravel()[diff[0]])
+    yg = y_gpu.ravel()
+    yr = y_ref.ravel()
+    idx = np.flatnonzero(yg != yr)
+    if idx.size == 0:
+        return 0.0, 1.0
+    ok, max_ulp, n_bad, first = check_y(yg[idx], yr[idx])
+    assert ok, "%s y outside tolerance at %d elements (max %.2f ulp; first flat index %d: gpu %04x oracle %04x)" % (
+        what, n_bad, max_ulp, idx[first], yg[idx[first]], yr[idx[first]])
+    return float(ulp_diff(yg[idx], yr[idx]).max()), 1.0 - idx.size / yg.size

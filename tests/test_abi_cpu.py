@@ -1,0 +1,195 @@
+"""The C-ABI library on the CPU (no GPU here): it loads, exports every entry
+point include/resnorm.h declares, and rejects every invalid argument on the
+host with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "resnorm.h")
+
+
+@pytest.fixture(scope="module")
+def rn():
+    import rmsnorm_diffusion_transformers_amd as rn
+    return rn
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                                 r"([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("resnorm_fused_fwd", "norm_scale_shift_fwd", "rn_last_error",
+              "rn_describe_launch", "rn_version"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol(rn):
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), "librnorm.so does not export %s" % name
+
+
+def test_version(rn):
+    assert "gfx950" in rn.version()
+
+
+# Fake, 16-byte aligned, non-overlapping "device" addresses: validation never
+# dereferences them and every call below fails before any device work.
+A = 1 << 40
+STRIDE = 1 << 32
+
+
+def addr(i):
+    return A + i * STRIDE
+
+
+def fused(rn, **kw):
+    args = dict(y=addr(0), residual_out=addr(1), x=addr(2), residual=addr(3), gate=addr(4),
+                weight=None, bias=None, scale=addr(7), shift=addr(8), B=1, L=16, D=5120,
+                flags=rn.RN_GATE, gate_layout=(rn.RN_BCAST, 0), ss_layout=(rn.RN_BCAST, 0),
+                eps=1e-6)
+    args.update(kw)
+    st = rn._lib.resnorm_fused_fwd(args["y"], args["residual_out"], args["x"], args["residual"],
+                                   args["gate"], args["weight"], args["bias"], args["scale"],
+                                   args["shift"], args["B"], args["L"], args["D"], args["flags"],
+                                   rn._layout(args["gate_layout"]), rn._layout(args["ss_layout"]),
+                                   args["eps"], None)
+    return st, rn.last_error()
+
+
+def nss(rn, **kw):
+    args = dict(y=addr(0), x=addr(2), weight=None, bias=None, scale=addr(7), shift=addr(8), B=1,
+                L=16, D=5120, flags=0, ss_layout=(rn.RN_BCAST, 0), eps=1e-6)
+    args.update(kw)
+    st = rn._lib.norm_scale_shift_fwd(args["y"], args["x"], args["weight"], args["bias"],
+                                      args["scale"], args["shift"], args["B"], args["L"],
+                                      args["D"], args["flags"], rn._layout(args["ss_layout"]),
+                                      args["eps"], None)
+    return st, rn.last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(y=None), 1, "y is NULL"),
+    (dict(x=None), 1, "x is NULL"),
+    (dict(residual=None), 1, "residual is NULL"),
+    (dict(residual_out=None), 1, "residual_out is NULL"),
+    (dict(scale=None), 1, "scale is NULL"),
+    (dict(shift=None), 1, "shift is NULL"),
+    (dict(gate=None), 1, "RN_GATE set but gate is NULL"),
+    (dict(flags=0), 1, "gate given but RN_GATE not set"),
+    (dict(weight=addr(5)), 1, "weight given"),
+    (dict(flags=2 | 4), 1, "RN_WEIGHT set but weight is NULL"),
+    (dict(flags=2 | 8, bias=addr(6)), 1, "RN_BIAS requires RN_WEIGHT"),
+    (dict(flags=2 | 4 | 8, weight=addr(5)), 1, "RN_BIAS set but bias is NULL"),
+    (dict(flags=2 | 64), 1, "unknown flag"),
+    (dict(D=5121), 1, "multiple of 8"),
+    (dict(D=0), 1, "multiple of 8"),
+    (dict(D=4), 1, "multiple of 8"),
+    (dict(D=16392), 2, "RN_D_MAX"),
+    (dict(B=-1), 1, "negative"),
+    (dict(L=-5), 1, "negative"),
+    (dict(B=1 << 20, L=1 << 12), 2, "2^31"),
+    (dict(eps=-1e-6), 1, "eps"),
+    (dict(eps=float("nan")), 1, "eps"),
+    (dict(eps=float("inf")), 1, "eps"),
+    (dict(x=addr(2) + 8), 1, "x is not 16-byte aligned"),
+    (dict(gate=addr(4) + 2), 1, "gate is not 16-byte aligned"),
+    (dict(gate_layout=(7, 0)), 1, "gate layout kind"),
+    (dict(ss_layout=(-1, 0)), 1, "scale/shift layout kind"),
+    (dict(ss_layout=(2, 0)), 1, "frames >= 1"),
+    (dict(ss_layout=(2, 5)), 1, "L % frames"),
+    (dict(gate_layout=(2, 3)), 1, "L % frames"),
+    (dict(y=addr(2) + 16), 1, "y overlaps x"),
+    (dict(y=addr(3)), 1, "y overlaps residual"),
+    (dict(residual_out=addr(2)), 1, "residual_out overlaps x"),
+    (dict(residual_out=addr(0)), 1, "overlaps"),
+    (dict(y=addr(7)), 1, "y overlaps scale"),
+    (dict(residual_out=addr(3) + 32), 1, "residual_out overlaps residual"),
+])
+def test_fused_rejects(rn, kw, status, msg):
+    st, err = fused(rn, **kw)
+    assert st == status, (st, err)
+    assert msg in err, err
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(flags=2), 1, "RN_GATE is only valid"),
+    (dict(y=None), 1, "y is NULL"),
+    (dict(D=12), 1, "multiple of 8"),
+    (dict(D=32768), 2, "RN_D_MAX"),
+    (dict(flags=4), 1, "RN_WEIGHT set but weight is NULL"),
+    (dict(ss_layout=(2, 3)), 1, "L % frames"),
+    (dict(y=addr(8)), 1, "y overlaps shift"),
+])
+def test_nss_rejects(rn, kw, status, msg):
+    st, err = nss(rn, **kw)
+    assert st == status, (st, err)
+    assert msg in err, err
+
+
+def test_empty_problem_is_ok_without_launch(rn):
+    assert fused(rn, B=0)[0] == 0
+    assert fused(rn, L=0)[0] == 0
+    assert nss(rn, B=3, L=0)[0] == 0
+    # an empty problem is still validated
+    assert fused(rn, B=0, D=7)[0] == 1
+
+
+def test_status_mapping_in_binding(rn):
+    with pytest.raises(rn.RnError) as e:
+        rn.resnorm_fused_fwd(addr(0), addr(1), addr(2), addr(3), None, None, None, addr(7),
+                             addr(8), 1, 16, 100, 0, stream=0)
+    assert e.value.status == rn.RN_EINVAL and "multiple of 8" in str(e.value)
+
+
+def test_describe_launch(rn):
+    info = rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True)
+    assert info["vec_per_lane"] == 10 and info["block_threads"] == 256
+    assert info["grid_blocks"] == 176400 // 4
+    assert rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)["vec_per_lane"] == 20
+    assert rn.describe_launch(1, 3, 8, 0, False)["vec_per_lane"] == 1
+    assert rn.describe_launch(1, 3, 1000, 0, False)["vec_per_lane"] == 2
+    assert rn.describe_launch(1, 3, 16384, 0, False)["vec_per_lane"] == 32
+    assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
+    with pytest.raises(rn.RnError):
+        rn.describe_launch(1, 3, 20000, 0, False)
+
+
+def test_layout_inference(rn):
+    import torch
+    B, L, D = 2, 12, 16
+    f = lambda *s: torch.empty(*s)
+    assert rn.infer_layout(f(D), B, L, D) == (rn.RN_BCAST, 0)
+    assert rn.infer_layout(f(1, D), B, L, D) == (rn.RN_BCAST, 0)
+    assert rn.infer_layout(f(1, 1, D), B, L, D) == (rn.RN_BCAST, 0)
+    assert rn.infer_layout(f(B, L, D), B, L, D) == (rn.RN_ROW, 0)
+    assert rn.infer_layout(f(B, 3, 1, D), B, L, D) == (rn.RN_FRAME, 3)
+    assert rn.infer_layout(f(B, D), B, L, D) == (rn.RN_FRAME, 1)
+    assert rn.infer_layout(f(B, 1, D), B, L, D) == (rn.RN_FRAME, 1)
+    with pytest.raises(ValueError):
+        rn.infer_layout(f(3, D), B, L, D)
+
+
+def test_no_cpu_path(rn):
+    import torch
+    x = torch.zeros(1, 2, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="no CPU path"):
+        rn.norm_scale_shift(x, None, None, torch.zeros(8, dtype=torch.bfloat16),
+                            torch.zeros(8, dtype=torch.bfloat16), "layer", 1e-6, stream=0)
+
+
+def test_inputs_may_share_memory(rn):
+    # scale and shift (read-only) may be the same buffer; an empty problem has
+    # no extents at all
+    st, err = nss(rn, B=0, shift=addr(7))
+    assert st == 0, err
+    st, err = fused(rn, B=0, shift=addr(7), gate=addr(7))
+    assert st == 0, err

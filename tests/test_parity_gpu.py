@@ -1,0 +1,341 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle on the GPU.
+
+Bar: residual_out bit-exact; y within max(2 bf16 ulps of the oracle's value,
+1e-2) element by element.  Inputs are the seeded synthetic workloads (the
+pages' shapes: sglang PR #36349, "Microbenchmark"; sglang PR #33144,
+"Accuracy Tests") and small random problems spanning every specialisation,
+layout and ragged row width.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import (compare_outputs, launch_workload, log, require_gpu, to_dev, to_host,
+                      workload_flags)
+from util import bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+BCAST, ROW, FRAME = 0, 1, 2
+THREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.fixture(scope="module")
+def rn():
+    require_gpu()
+    import rmsnorm_diffusion_transformers_amd as rn
+    return rn
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def _run_full(rn, orc, wl, check_rows=None):
+    import torch
+    log("workload %s: generating inputs" % wl.name)
+    inp = synth.make_inputs(wl, threads=THREADS)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    y = torch.empty_like(d["x"])
+    ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
+    log("workload %s: launching (B=%d L=%d D=%d)" % (wl.name, wl.B, wl.L, wl.D))
+    launch_workload(rn, wl, d, y, ro)
+    torch.cuda.synchronize()
+    yh = to_host(y)
+    roh = to_host(ro) if ro is not None else None
+    del d, y, ro
+    log("workload %s: oracle on %d rows x %d threads" % (wl.name, wl.R, THREADS))
+    y_ref, ro_ref, _ = orc.run_workload(wl, inp, threads=THREADS)
+    max_ulp, exact = compare_outputs(yh, y_ref, roh, ro_ref, wl.name)
+    log("workload %s: OK  y max err %.2f ulp, %.5f%% bit-identical" % (wl.name, max_ulp, 100 * exact))
+    return inp, yh, roh
+
+
+@pytest.mark.parametrize("name", ["fused_ln_b1_l16_d5120", "fused_rms_w_b2_l16_d10240"])
+def test_small_workloads_all_rows(rn, orc, name):
+    _run_full(rn, orc, synth.WORKLOADS[name])
+
+
+@pytest.mark.parametrize("name", ["fused_ln_b1_l90000_d5120", "fused_rms_w_b1_l90000_d10240",
+                                  "nss_ln_b1_l176400_d5120", "fused_ln_frame_b1_f49_l176400_d5120"])
+def test_full_size_workloads_all_rows(rn, orc, name):
+    """Every row of the full-size workloads, in the launch configuration the
+    benchmark times, against the oracle."""
+    _run_full(rn, orc, synth.WORKLOADS[name])
+
+
+def _small_problem(seed, fused, rms, gate_layout, aff, ss_layout, B, L, D):
+    R = B * L
+
+    def rows(lay):
+        return {BCAST: 1, ROW: R, FRAME: B * lay[1]}[lay[0]]
+
+    inp = {"x": synth.random_bf16((R, D), seed, 1)}
+    if fused:
+        inp["residual"] = synth.random_bf16((R, D), seed, 2)
+        if gate_layout is not None:
+            inp["gate"] = synth.random_bf16((rows(gate_layout), D), seed, 3, dist=synth.UNIFORM,
+                                            a=0.0, b=1.0)
+    if aff >= 1:
+        inp["weight"] = synth.random_bf16((D,), seed, 4, a=1.0, b=0.05)
+    if aff >= 2:
+        inp["bias"] = synth.random_bf16((D,), seed, 5, a=0.0, b=0.1)
+    inp["scale"] = synth.random_bf16((rows(ss_layout), D), seed, 6, a=0.0, b=0.1)
+    inp["shift"] = synth.random_bf16((rows(ss_layout), D), seed, 7, a=0.0, b=0.1)
+    return inp
+
+
+def _check_small(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D):
+    import torch
+    inp = _small_problem(seed, fused, rms, gate_layout, aff, ss_layout, B, L, D)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    flags = (rn.RN_RMS if rms else 0) | (rn.RN_WEIGHT if aff >= 1 else 0) | (rn.RN_BIAS if aff >= 2 else 0)
+    y = torch.empty_like(d["x"])
+    case = "seed=%d fused=%s rms=%s gate=%s aff=%d ss=%s B=%d L=%d D=%d" % (
+        seed, fused, rms, gate_layout, aff, ss_layout, B, L, D)
+    if fused:
+        if gate_layout is not None:
+            flags |= rn.RN_GATE
+        ro = torch.empty_like(d["x"])
+        rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d.get("gate"), d.get("weight"),
+                             d.get("bias"), d["scale"], d["shift"], B, L, D, flags,
+                             gate_layout or (BCAST, 0), ss_layout, 1e-6)
+        torch.cuda.synchronize()
+        y_ref, ro_ref, _ = orc.fused(inp["x"], inp["residual"], inp.get("gate"), inp.get("weight"),
+                                     inp.get("bias"), inp["scale"], inp["shift"], B, L, D, rms,
+                                     gate_layout or (BCAST, 0), ss_layout, 1e-6)
+        compare_outputs(to_host(y), y_ref, to_host(ro), ro_ref, case)
+    else:
+        rn.norm_scale_shift_fwd(y, d["x"], d.get("weight"), d.get("bias"), d["scale"], d["shift"],
+                                B, L, D, flags, ss_layout, 1e-6)
+        torch.cuda.synchronize()
+        y_ref, _ = orc.nss(inp["x"], inp.get("weight"), inp.get("bias"), inp["scale"],
+                           inp["shift"], B, L, D, rms, ss_layout, 1e-6)
+        compare_outputs(to_host(y), y_ref, what=case)
+
+
+LAYOUTS = [(BCAST, 0), (ROW, 0), (FRAME, 3)]
+WIDTHS = [8, 64, 136, 520, 1000, 4104, 5120, 8192, 8200, 10240, 16384]
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_specialisation_matrix(rn, orc, D):
+    """Every flag combination (is_rms x has_gate x affine none/weight/weight+bias,
+    fused and norm-only) at one row width, cycling through the layouts; B=2,
+    L=6, F=3.  Widths include exact fits of each register-cache width and
+    ragged rows whose tail lanes are masked."""
+    log("specialisation matrix D=%d" % D)
+    B, L = 2, 6
+    k = 0
+    for rms in (False, True):
+        for aff in (0, 1, 2):
+            for gate in (True, False):
+                gl = LAYOUTS[k % 3] if gate else None
+                sl = LAYOUTS[(k // 3 + k) % 3]
+                _check_small(rn, orc, 100 + k + D, True, rms, gl, aff, sl, B, L, D)
+                k += 1
+            _check_small(rn, orc, 200 + k + D, False, rms, None, aff, LAYOUTS[k % 3], B, L, D)
+            k += 1
+
+
+def test_all_layout_pairs(rn, orc):
+    """Every gate layout x scale/shift layout pair, both norms, several frame counts."""
+    for rms in (False, True):
+        for gl in LAYOUTS + [(FRAME, 1), (FRAME, 6)]:
+            for sl in LAYOUTS + [(FRAME, 2), (FRAME, 6)]:
+                _check_small(rn, orc, 7, True, rms, gl, 0, sl, 2, 6, 64)
+                _check_small(rn, orc, 8, True, rms, gl, 2, sl, 3, 12, 320)
+
+
+def test_residual_every_bf16_x(rn, orc):
+    """residual_out for every bf16 bit pattern of x against 64 residual values
+    and 16 gates (per-row gate layout): bit-exact with the oracle; NaN outputs
+    compared as NaN."""
+    import torch
+    xs = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    rng = np.random.default_rng(11)
+    res_vals = rng.integers(0, 1 << 16, 256).astype(np.uint16)
+    res_vals = res_vals[(res_vals & 0x7F80) != 0x7F80][:64]
+    gates = np.concatenate([np.array([0x0000, 0x3F80, 0x3F00, 0x3F40], np.uint16),
+                            rng.integers(0x3C00, 0x3F80, 12).astype(np.uint16)])
+    D = 1024
+    X = np.tile(xs, len(res_vals) * len(gates)).reshape(-1, D)
+    Rr = np.repeat(np.repeat(res_vals, len(xs)), len(gates)).reshape(-1, D)
+    G = np.tile(np.repeat(gates, len(xs)), len(res_vals)).reshape(-1, D)
+    R = X.shape[0]
+    log("residual brute force: %d rows of %d" % (R, D))
+    zeros = np.zeros((1, D), np.uint16)
+    dx, dr, dg, dz = to_dev(X), to_dev(Rr), to_dev(G), to_dev(zeros)
+    y = torch.empty_like(dx)
+    ro = torch.empty_like(dx)
+    rn.resnorm_fused_fwd(y, ro, dx, dr, dg, None, None, dz, dz, 1, R, D, rn.RN_GATE,
+                         (ROW, 0), (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    got = to_host(ro)
+    ref = orc.residual(Rr, G, X)
+    gnan = (got & 0x7FFF) > 0x7F80
+    rnan = (ref & 0x7FFF) > 0x7F80
+    bad = (gnan != rnan) | (~gnan & (got != ref))
+    assert not bad.any(), "x %04x res %04x gate %04x: gpu %04x oracle %04x" % (
+        X[bad][0], Rr[bad][0], G[bad][0], got[bad][0], ref[bad][0])
+
+
+def test_determinism_permutation_and_norm_of_residual(rn, orc):
+    """Reruns are bitwise identical; permuting rows permutes the outputs bit-
+    exactly (broadcast layouts); the fused y equals the norm-only op applied to
+    the fused op's residual_out, bit-exactly."""
+    import torch
+    B, L, D = 1, 512, 5120
+    inp = _small_problem(21, True, False, (BCAST, 0), 0, (BCAST, 0), B, L, D)
+    d = {k: to_dev(v) for k, v in inp.items()}
+
+    def run(dd):
+        y = torch.empty_like(dd["x"])
+        ro = torch.empty_like(dd["x"])
+        rn.resnorm_fused_fwd(y, ro, dd["x"], dd["residual"], dd["gate"], None, None, dd["scale"],
+                             dd["shift"], B, L, D, rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6)
+        return y, ro
+
+    y1, ro1 = run(d)
+    y2, ro2 = run(d)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(ro1.view(torch.int16), ro2.view(torch.int16))
+    perm = np.random.default_rng(3).permutation(L)
+    dp = dict(d)
+    dp["x"] = to_dev(inp["x"][perm])
+    dp["residual"] = to_dev(inp["residual"][perm])
+    y3, ro3 = run(dp)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y3), to_host(y1)[perm])
+    assert np.array_equal(to_host(ro3), to_host(ro1)[perm])
+    yn = torch.empty_like(y1)
+    rn.norm_scale_shift_fwd(yn, ro1, None, None, d["scale"], d["shift"], B, L, D, 0, (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(yn.view(torch.int16), y1.view(torch.int16))
+
+
+def test_in_place_aliasing(rn, orc):
+    """y == x and residual_out == residual give the out-of-place results."""
+    import torch
+    B, L, D = 2, 40, 10240
+    inp = _small_problem(31, True, True, (BCAST, 0), 1, (ROW, 0), B, L, D)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    flags = rn.RN_RMS | rn.RN_GATE | rn.RN_WEIGHT
+    y = torch.empty_like(d["x"])
+    ro = torch.empty_like(d["x"])
+    rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d["gate"], d["weight"], None, d["scale"],
+                         d["shift"], B, L, D, flags, (BCAST, 0), (ROW, 0), 1e-6)
+    xi, ri = d["x"].clone(), d["residual"].clone()
+    rn.resnorm_fused_fwd(xi, ri, xi, ri, d["gate"], d["weight"], None, d["scale"], d["shift"],
+                         B, L, D, flags, (BCAST, 0), (ROW, 0), 1e-6)
+    xn = d["x"].clone()
+    yn = torch.empty_like(xn)
+    rn.norm_scale_shift_fwd(yn, xn, d["weight"], None, d["scale"], d["shift"], B, L, D,
+                            rn.RN_RMS | rn.RN_WEIGHT, (ROW, 0), 1e-6)
+    rn.norm_scale_shift_fwd(xn, xn, d["weight"], None, d["scale"], d["shift"], B, L, D,
+                            rn.RN_RMS | rn.RN_WEIGHT, (ROW, 0), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.equal(xi.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(ri.view(torch.int16), ro.view(torch.int16))
+    assert torch.equal(xn.view(torch.int16), yn.view(torch.int16))
+
+
+@pytest.mark.parametrize("D", [8, 1000, 8200])
+def test_ragged_rows_leave_neighbours_untouched(rn, orc, D):
+    """Outputs are written only inside their rows: guard rows after the last
+    row (and the whole buffers beyond it) keep their contents, for row widths
+    whose tail lanes are masked by the per-row buffer range."""
+    import torch
+    B, L = 1, 7
+    inp = _small_problem(41, True, False, (BCAST, 0), 0, (BCAST, 0), B, L, D)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    guard = 5
+    y_buf = torch.full((L + guard, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    ro_buf = torch.full((L + guard, D), -3.0, dtype=torch.bfloat16, device="cuda")
+    rn.resnorm_fused_fwd(y_buf[:L], ro_buf[:L], d["x"], d["residual"], d["gate"], None, None,
+                         d["scale"], d["shift"], B, L, D, rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.all(y_buf[L:] == 3.0) and torch.all(ro_buf[L:] == -3.0)
+    y_ref, ro_ref, _ = orc.fused(inp["x"], inp["residual"], inp["gate"], None, None, inp["scale"],
+                                 inp["shift"], B, L, D, False)
+    compare_outputs(to_host(y_buf[:L]), y_ref, to_host(ro_buf[:L]), ro_ref, "ragged D=%d" % D)
+
+
+def test_empty_and_side_stream(rn, orc):
+    """B*L = 0 enqueues nothing; a call on a non-default stream is ordered on it."""
+    import torch
+    D = 256
+    z = torch.zeros((1, D), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((4, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    rn.norm_scale_shift_fwd(y, z, None, None, z, z, 0, 4, D, 0, (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    inp = _small_problem(51, False, False, None, 0, (BCAST, 0), 1, 64, D)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        d = {k: to_dev(v) for k, v in inp.items()}
+        y = torch.empty_like(d["x"])
+        rn.norm_scale_shift_fwd(y, d["x"], None, None, d["scale"], d["shift"], 1, 64, D, 0,
+                                (BCAST, 0), 1e-6, stream=s)
+    s.synchronize()
+    y_ref, _ = orc.nss(inp["x"], None, None, inp["scale"], inp["shift"], 1, 64, D, False)
+    compare_outputs(to_host(y), y_ref, what="side stream")
+
+
+def test_gpu_norm_invariants(rn, orc):
+    """Pure-norm GPU outputs (scale = shift = 0, no affine) at D >= 512.
+
+    The exact normalised row t has mean 0 and variance 1 (RMS 1) up to the eps
+    term; the oracle pins that on t to 1e-3.  A bf16 output y differs from t by
+    at most half an ulp, i.e. |y - t| <= 2^-8 |t|, so its row variance can move
+    by up to (2 * 2^-8 + 2^-16) * mean(t^2) and its mean by 2^-8 * mean|t| --
+    and it does, systematically, because y tends to stay on the input's own bf16
+    grid when the row scale is close to 1.  So the GPU rows are held to those
+    bounds (plus 1e-3), and their moments must also agree with the moments of
+    the oracle's bf16 rows to 1e-3."""
+    import torch
+    q = 2.0 ** -8
+    for D in (512, 5120, 10240):
+        L = 64
+        x = synth.random_bf16((L, D), 61, 1)
+        z = np.zeros((1, D), np.uint16)
+        dx, dz = to_dev(x), to_dev(z)
+        for rms in (False, True):
+            y = torch.empty_like(dx)
+            rn.norm_scale_shift_fwd(y, dx, None, None, dz, dz, 1, L, D,
+                                    rn.RN_RMS if rms else 0, (BCAST, 0), 1e-6)
+            torch.cuda.synchronize()
+            t = bf16_to_f64(to_host(y))
+            ref = bf16_to_f64(orc.nss(x, None, None, z, z, 1, L, D, rms)[0])
+            if rms:
+                ms = (t * t).mean(1)
+                assert np.all(np.abs(ms - 1) <= 2 * q + q * q + 1e-3)
+                assert np.all(np.abs(ms - (ref * ref).mean(1)) <= 1e-3)
+            else:
+                assert np.all(np.abs(t.mean(1)) <= q * np.abs(t).mean(1) + 1e-3)
+                assert np.all(np.abs(t.var(1) - 1) <= 2 * q + q * q + 1e-3)
+                assert np.all(np.abs(t.mean(1) - ref.mean(1)) <= 1e-3)
+                assert np.all(np.abs(t.var(1) - ref.var(1)) <= 1e-3)
+
+
+def test_mean_offset_rows(rn, orc):
+    """Rows with a large common offset (|mean| >> std) stay within tolerance: the
+    kernel centres the register-resident row before squaring."""
+    import torch
+    D, L = 5120, 32
+    base = synth.random_bf16((L, D), 71, 1)
+    xf = (base.astype(np.uint32) << 16).view(np.float32) + np.float32(300.0)
+    x = ((xf.view(np.uint32) + 0x7FFF + ((xf.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    sc = synth.random_bf16((1, D), 71, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 71, 7, a=0.0, b=0.1)
+    y = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+    rn.norm_scale_shift_fwd(y, to_dev(x), None, None, to_dev(sc), to_dev(sh), 1, L, D, 0,
+                            (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    y_ref, _ = orc.nss(x, None, None, sc, sh, 1, L, D, False)
+    compare_outputs(to_host(y), y_ref, what="mean offset 300")
