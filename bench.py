@@ -33,7 +33,7 @@ HEADLINE = "fused_ln_frame_b1_f49_l176400_d5120"
 COMPANION = "nss_ln_b1_l176400_d5120"
 KERNEL_SOURCES = ["rmsnorm_diffusion_transformers_amd/csrc/rn_row_kernel.hpp",
                   "rmsnorm_diffusion_transformers_amd/csrc/rn_args.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(msg):
@@ -53,13 +53,14 @@ def measured_traffic(workload: str):
     on the current kernel source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
+            lines = [ln.split() for ln in f if ln.startswith("workload ")]
+    except OSError:
         return None
-    rec = t.get("workloads", {}).get(workload)
-    if not rec or rec.get("kernel_digest") != kernel_digest():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for toks in lines:
+        rec = dict(zip(toks[0::2], toks[1::2]))
+        if rec.get("workload") == workload and rec.get("kernel_digest") == kernel_digest():
+            return int(rec["hbm_bytes_per_launch"])
+    return None
 
 
 def threads() -> int:
@@ -104,13 +105,18 @@ def time_workload(rn, wl, steps, warmup, dev):
     return ms, wall
 
 
+def flags_of(rn, wl):
+    f = (rn.RN_RMS if wl.is_rms else 0) | (rn.RN_WEIGHT if wl.has_weight else 0) | \
+        (rn.RN_BIAS if wl.has_bias else 0)
+    if wl.op == "fused" and wl.gate_layout is not None:
+        f |= rn.RN_GATE
+    return f
+
+
 def launch_workload(rn, wl, d, y, ro, stream):
     """One pass of the workload through the C entry points."""
-    flags = (rn.RN_RMS if wl.is_rms else 0) | (rn.RN_WEIGHT if wl.has_weight else 0) | \
-        (rn.RN_BIAS if wl.has_bias else 0)
+    flags = flags_of(rn, wl)
     if wl.op == "fused":
-        if wl.gate_layout is not None:
-            flags |= rn.RN_GATE
         rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d.get("gate"), d.get("weight"),
                              d.get("bias"), d["scale"], d["shift"], wl.B, wl.L, wl.D, flags,
                              wl.gate_layout or (0, 0), wl.ss_layout, wl.eps, stream)
@@ -119,9 +125,11 @@ def launch_workload(rn, wl, d, y, ro, stream):
                                 d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps, stream)
 
 
-def calibrate(steps, warmup, dev):
+def copy_reference(steps, warmup, dev):
     """A plain elementwise copy (torch.neg on bf16: reads N bytes, writes N
-    bytes) on a tensor of the headline's activation size."""
+    bytes) on a tensor of the headline's activation size: the rocprof counter
+    calibration kernel, and a practical read+write bandwidth reference on the
+    same GPU in the same run."""
     import torch
     n = 176400 * 5120
     x = torch.randn(n, device=dev).to(torch.bfloat16)
@@ -136,9 +144,15 @@ def calibrate(steps, warmup, dev):
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
-    out = {"metric": "elementwise copy (calibration)", "bytes_read": 2 * n, "bytes_written": 2 * n,
-           "ms": ms, "GB/s": 4 * n / ms / 1e6}
-    print(json.dumps(out), flush=True)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"kernel": "torch.neg bf16 (1 read + 1 write stream)", "bytes_per_launch": 4 * n,
+            "ms_per_launch": round(ms, 5), "GB/s": round(4 * n / ms / 1e6, 1),
+            "frac": round(4 * n / ms / 1e6 / HBM_PEAK_GBS, 4)}
+
+
+def calibrate(steps, warmup, dev):
+    print(json.dumps(copy_reference(steps, warmup, dev)), flush=True)
 
 
 def cpu_baseline(wl):
@@ -225,7 +239,9 @@ def main():
                            "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
                            "algorithmic_bytes": wc.algorithmic_bytes(),
                            "traffic": measured_traffic(wc.name)})
-    info = rn.describe_launch(wl.B, wl.L, wl.D, 0, wl.op == "fused")
+    info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused")
+    ref = copy_reference(args.steps, args.warmup, dev)
+    log("copy reference: %.1f GB/s" % ref["GB/s"])
     line = {
         "metric": "fused residual-norm HBM GB/s and % of peak, bf16 L=176400 D=5120",
         "value": round(gbs, 1),
@@ -247,6 +263,7 @@ def main():
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)},
         "wall_s_timed_region": round(wall, 4),
         "companions": companions,
+        "copy_reference": ref,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)

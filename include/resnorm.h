@@ -121,10 +121,12 @@ rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const
 const char* rn_last_error(void);
 
 /* Launch shape the library would use for a problem (host-only query; no
- * device work, usable without a GPU): vectors of 8 bf16 per lane, waves per
- * workgroup, rows per workgroup, workgroup size and grid size. */
+ * device work, usable without a GPU): 16-byte vectors per lane and operand,
+ * waves per activation row, waves and rows per workgroup, workgroup size and
+ * grid size.  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd (0). */
 typedef struct {
   int32_t vec_per_lane;
+  int32_t waves_per_row;
   int32_t waves_per_block;
   int32_t rows_per_block;
   int32_t block_threads;

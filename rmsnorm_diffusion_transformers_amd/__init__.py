@@ -39,7 +39,8 @@ class rn_layout(ctypes.Structure):
 
 
 class rn_launch_info(ctypes.Structure):
-    _fields_ = [("vec_per_lane", ctypes.c_int32), ("waves_per_block", ctypes.c_int32),
+    _fields_ = [("vec_per_lane", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
+                ("waves_per_block", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("block_threads", ctypes.c_int32),
                 ("grid_blocks", ctypes.c_int64)]
 

@@ -96,11 +96,28 @@ rn_status check_shape(int64_t B, int64_t L, int64_t D, uint32_t flags, bool fuse
   return RN_OK;
 }
 
-int vec_index_for(int64_t D) {
-  const int64_t need = (D / 8 + rn::kWaveSize - 1) / rn::kWaveSize;
-  for (int i = 0; i < rn::kNumVecWidths; ++i)
-    if (rn::kVecWidths[i] >= need) return i;
-  return -1;
+// Row operands a kernel loads per row (each VPT vectors per lane).
+int row_operands(uint32_t flags, bool fused) {
+  int n = 3;  // x, scale, shift
+  if (fused) n += 1 + ((flags & RN_GATE) ? 1 : 0);
+  if (flags & RN_WEIGHT) n += 1;
+  if (flags & RN_BIAS) n += 1;
+  return n;
+}
+
+// First compiled shape that covers a row of D elements within the register
+// budget; else the widest shape that covers it; -1 if none does.
+int shape_for(int64_t D, uint32_t flags, bool fused) {
+  const int64_t nvec = D / 8;
+  const int ops = row_operands(flags, fused);
+  int fallback = -1;
+  for (int i = 0; i < rn::kNumShapes; ++i) {
+    const rn::Shape s = rn::kShapes[i];
+    if ((int64_t)rn::kWaveSize * s.w * s.vpt < nvec) continue;
+    if (s.vpt * ops <= rn::kVgprBudget) return i;
+    if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
+  }
+  return fallback;
 }
 
 rn_status validate(const Problem& p) {
@@ -188,7 +205,7 @@ rn_status run(const Problem& p, void* stream) {
   if (st != RN_OK) return st;
   const int64_t R = p.B * p.L;
   if (R == 0) return RN_OK;
-  const int vi = vec_index_for(p.D);
+  const int vi = shape_for(p.D, p.flags, p.fused);
   rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
   if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
 
@@ -215,7 +232,8 @@ rn_status run(const Problem& p, void* stream) {
   a.ss_tokens_per_frame = tokens_per_frame(p.ss_layout, p.L);
   if (!(p.flags & RN_GATE)) a.gate_kind = RN_BCAST;
 
-  const int64_t blocks = (R + rn::kWavesPerBlock - 1) / rn::kWavesPerBlock;
+  const int64_t rows_per_block = rn::kWavesPerBlock / rn::kShapes[vi].w;
+  const int64_t blocks = (R + rows_per_block - 1) / rows_per_block;
   void* args[] = {&a};
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)blocks), dim3(rn::kBlockThreads), args, 0,
                                  (hipStream_t)stream);
@@ -252,13 +270,15 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   if (!info) return fail(RN_EINVAL, "info is NULL");
   rn_status st = check_shape(B, L, D, flags, fused != 0);
   if (st != RN_OK) return st;
-  const int vi = vec_index_for(D);
-  if (vi < 0) return fail(RN_EUNSUPPORTED, "no register-cache width covers D=%lld", (long long)D);
-  info->vec_per_lane = rn::kVecWidths[vi];
+  const int vi = shape_for(D, flags, fused != 0);
+  if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
+  const rn::Shape s = rn::kShapes[vi];
+  info->vec_per_lane = s.vpt;
+  info->waves_per_row = s.w;
   info->waves_per_block = rn::kWavesPerBlock;
-  info->rows_per_block = rn::kWavesPerBlock;
+  info->rows_per_block = rn::kWavesPerBlock / s.w;
   info->block_threads = rn::kBlockThreads;
-  info->grid_blocks = (B * L + rn::kWavesPerBlock - 1) / rn::kWavesPerBlock;
+  info->grid_blocks = (B * L + info->rows_per_block - 1) / info->rows_per_block;
   return RN_OK;
 }
 

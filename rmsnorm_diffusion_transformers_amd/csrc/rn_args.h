@@ -6,17 +6,31 @@
 
 namespace rn {
 
-// One workgroup = kWavesPerBlock waves; each wave owns one activation row.
+// A 256-thread workgroup of kWavesPerBlock waves.  W waves own one activation
+// row (W = 1, 2 or 4), so a workgroup holds kWavesPerBlock / W rows.
 constexpr int kWaveSize = 64;
 constexpr int kWavesPerBlock = 4;
 constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
 
-// Per-lane register-cache widths (16-byte vectors of 8 bf16 per lane) that are
-// compiled.  A row of D columns needs ceil(D / 8 / 64) vectors per lane; the
-// launcher picks the smallest compiled width that covers it and the tail
-// lanes are masked.  32 covers D = 16384.
-constexpr int kVecWidths[] = {1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 20, 24, 32};
-constexpr int kNumVecWidths = sizeof(kVecWidths) / sizeof(kVecWidths[0]);
+// Compiled shapes: (waves per row W, 16-byte vectors per lane VPT).  One wave
+// holds W-th of a row, VPT vectors of 8 bf16 per lane per operand, so a shape
+// covers rows of up to 64 * W * VPT vectors (D = 512 * W * VPT); tail lanes of
+// shorter rows are masked.  The launcher takes the first shape, in this
+// order, that covers D and keeps VPT * (row operands loaded) <= kVgprBudget.
+struct Shape {
+  int w;
+  int vpt;
+};
+constexpr Shape kShapes[] = {{1, 1}, {1, 2}, {1, 3}, {1, 4},  {1, 5}, {1, 6}, {1, 8}, {1, 10},
+                             {2, 6}, {2, 8}, {2, 10}, {4, 4}, {4, 5}, {4, 6}, {4, 8}};
+constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
+// VPT x operands per row kept below this: all loads of a row are in flight at
+// once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough
+// to saturate HBM with this access pattern.
+constexpr int kVgprBudget = 52;
+// Spacing of loads / stores, in units of 8 cycles (s_nop 7).
+constexpr int kPaceLoads = 0;
+constexpr int kPaceStores = 2;
 
 // Kernel arguments (one struct, passed by value).
 struct RowArgs {
@@ -49,10 +63,10 @@ typedef void (*KernelFn)(RowArgs);
 enum { kAffNone = 0, kAffWeight = 1, kAffWeightBias = 2 };
 
 // Kernel lookup; each returns nullptr for an uncompiled combination.
-// vec_index indexes kVecWidths.
-KernelFn fused_ln_kernel(bool gate, int aff, int vec_index);
-KernelFn fused_rms_kernel(bool gate, int aff, int vec_index);
-KernelFn nss_ln_kernel(int aff, int vec_index);
-KernelFn nss_rms_kernel(int aff, int vec_index);
+// shape indexes kShapes.
+KernelFn fused_ln_kernel(bool gate, int aff, int shape);
+KernelFn fused_rms_kernel(bool gate, int aff, int shape);
+KernelFn nss_ln_kernel(int aff, int shape);
+KernelFn nss_rms_kernel(int aff, int shape);
 
 }  // namespace rn

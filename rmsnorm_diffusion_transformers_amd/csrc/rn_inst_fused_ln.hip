@@ -1,17 +1,17 @@
-// Compiled specialisations: fused ln (every gate / affine / register-cache width).
+// Compiled specialisations: fused ln (every gate / affine / compiled shape).
 #include "rn_row_kernel.hpp"
 
 namespace rn {
 
-KernelFn fused_ln_kernel(bool gate, int aff, int vec_index) {
+KernelFn fused_ln_kernel(bool gate, int aff, int shape) {
   if (gate) {
-    if (aff == kAffNone) return kernel_for_width<false, true, true, kAffNone>(vec_index);
-    if (aff == kAffWeight) return kernel_for_width<false, true, true, kAffWeight>(vec_index);
-    if (aff == kAffWeightBias) return kernel_for_width<false, true, true, kAffWeightBias>(vec_index);
+    if (aff == kAffNone) return kernel_for_shape<false, true, true, kAffNone>(shape);
+    if (aff == kAffWeight) return kernel_for_shape<false, true, true, kAffWeight>(shape);
+    if (aff == kAffWeightBias) return kernel_for_shape<false, true, true, kAffWeightBias>(shape);
   } else {
-    if (aff == kAffNone) return kernel_for_width<false, true, false, kAffNone>(vec_index);
-    if (aff == kAffWeight) return kernel_for_width<false, true, false, kAffWeight>(vec_index);
-    if (aff == kAffWeightBias) return kernel_for_width<false, true, false, kAffWeightBias>(vec_index);
+    if (aff == kAffNone) return kernel_for_shape<false, true, false, kAffNone>(shape);
+    if (aff == kAffWeight) return kernel_for_shape<false, true, false, kAffWeight>(shape);
+    if (aff == kAffWeightBias) return kernel_for_shape<false, true, false, kAffWeightBias>(shape);
   }
   return nullptr;
 }

@@ -1,12 +1,12 @@
-// Compiled specialisations: nss rms (every affine / register-cache width).
+// Compiled specialisations: nss rms (every affine / compiled shape).
 #include "rn_row_kernel.hpp"
 
 namespace rn {
 
-KernelFn nss_rms_kernel(int aff, int vec_index) {
-  if (aff == kAffNone) return kernel_for_width<true, false, false, kAffNone>(vec_index);
-  if (aff == kAffWeight) return kernel_for_width<true, false, false, kAffWeight>(vec_index);
-  if (aff == kAffWeightBias) return kernel_for_width<true, false, false, kAffWeightBias>(vec_index);
+KernelFn nss_rms_kernel(int aff, int shape) {
+  if (aff == kAffNone) return kernel_for_shape<true, false, false, kAffNone>(shape);
+  if (aff == kAffWeight) return kernel_for_shape<true, false, false, kAffWeight>(shape);
+  if (aff == kAffWeightBias) return kernel_for_shape<true, false, false, kAffWeightBias>(shape);
   return nullptr;
 }
 

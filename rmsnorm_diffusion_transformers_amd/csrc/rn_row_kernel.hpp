@@ -1,28 +1,6 @@
 // rn_row_kernel.hpp -- gfx950 row kernel for the fused residual + gate +
 // LayerNorm/RMSNorm + scale/shift operation and its norm-only variant.
 //
-// Design (bandwidth-bound; no matrix cores -- nothing here is a contraction):
-//   * one wave64 per activation row, four rows per 256-thread workgroup; the
-//     row index is wave-uniform, so every per-row quantity (base addresses,
-//     modulation row, statistics) lives in scalar registers and the waves of a
-//     workgroup never synchronise with each other;
-//   * every global access is a 128-bit buffer load/store (8 bf16 per lane) on
-//     a per-row buffer descriptor whose range is exactly the row, so lanes past
-//     the end of a ragged row read zeros and their stores are dropped by the
-//     hardware range check;
-//   * the streamed tensors (x, residual in; y, residual_out out) use the
-//     non-temporal cache policy; modulation rows (gate/scale/shift/weight/bias)
-//     use the default policy so that broadcast and per-frame rows stay in L2;
-//   * the whole row stays in VGPRs (bf16-packed) between the statistics and
-//     the normalise/modulate epilogue, so HBM sees each byte once;
-//   * statistics in fp32: LayerNorm takes the mean, then the centred sum of
-//     squares over the register-resident row (two wave reductions); RMSNorm
-//     takes the sum of squares.  Wave reductions are DPP (xor 1, xor 2, half
-//     row mirror, row mirror) then the gfx950 permlane16/permlane32 swaps;
-//     every lane ends with the bit-identical total;
-//   * fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even, denormals
-//     kept -- fp32 denormal mode is IEEE in these kernels).
-//
 // The operation (sglang PR #36349, "Microbenchmark": operand order of
 // flydsl_fused_residual_norm_scale_shift / flydsl_norm_scale_shift; layouts
 // and specialisations from sglang PR #33144, "Modifications"):
@@ -32,6 +10,36 @@
 //                = h * rsqrt(mean(h^2) + eps)        [RMSNorm]
 //   n            = n * weight (+ bias)
 //   y            = bf16(n * (1 + scale) + shift)
+//
+// Design (HBM-bound; no matrix cores -- nothing here is a contraction):
+//   * W wave64s own one activation row (W = 1, 2 or 4); a 256-thread
+//     workgroup holds 4 / W rows.  Row indices are wave-uniform, so per-row
+//     quantities (descriptors, modulation row, statistics) live in SGPRs.
+//   * Every global access is a 128-bit buffer load/store (8 bf16 per lane) on
+//     a per-row buffer descriptor whose range is exactly the row: lanes past
+//     the end of a ragged row read zeros and their stores are dropped by the
+//     hardware range check.
+//   * All loads of a row -- x, residual, gate, weight, bias, scale, shift --
+//     are issued before its first store.  Loads and stores share the in-order
+//     vmcnt counter on gfx9, so a load issued after a store could only be
+//     waited for together with that store; issuing every load first keeps the
+//     store latency off the critical path.
+//   * Loads are issued PL x 8 cycles apart and stores PS x 8 cycles apart
+//     (s_nop): measured on MI355X, back-to-back bursts of 128-bit stores from
+//     every wave stream several percent slower than lightly spaced ones.
+//   * Streamed tensors (x, residual in; y, residual_out out) use the
+//     non-temporal policy; modulation rows use the default policy, so the
+//     broadcast and per-frame rows stay resident in L2.
+//   * The row stays in VGPRs (bf16-packed) between the statistics and the
+//     epilogue, so HBM sees each byte once.
+//   * Statistics in fp32.  LayerNorm: the mean, then the centred sum of squares
+//     over the register-resident row.  RMSNorm: the sum of squares.  Wave
+//     reductions are DPP (xor 1, xor 2, half-row mirror, row mirror) then the
+//     gfx950 permlane16/permlane32 swaps; with W > 1 the per-wave totals are
+//     combined through LDS in a fixed order.  Every lane and every wave of a
+//     row ends with the bit-identical total.
+//   * fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even; fp32
+//     denormals are kept in these kernels).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -57,14 +65,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, uin
                                            kRsrcWord3);
 }
 
-template <int POLICY>
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+// Spacing after a memory instruction; the scheduling barrier keeps the
+// compiler from regrouping the instructions into a burst.
+template <int PACE>
+__device__ __forceinline__ void pace() {
+  if constexpr (PACE > 0) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < PACE; ++i) asm volatile("s_nop 7");
+  }
 }
 
-template <int POLICY>
+template <int POLICY, int PACE>
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY));
+  pace<PACE>();
+  return v;
+}
+
+template <int POLICY, int PACE>
 __device__ __forceinline__ void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, POLICY);
+  pace<PACE>();
 }
 
 // bf16 pair <-> fp32: the low half of a dword is the element at the lower
@@ -99,6 +121,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Total over the W waves of one row.  Each wave's total goes to LDS; after the
+// barrier every wave of the row adds the W partials in the same order.
+template <int W>
+__device__ __forceinline__ float row_sum(float v, float* red, uint32_t wave, uint32_t slot) {
+  v = wave_sum(v);
+  if constexpr (W > 1) {
+    if ((threadIdx.x & (kWaveSize - 1)) == 0) red[wave] = v;
+    __syncthreads();
+    v = red[slot * W];
+#pragma unroll
+    for (int p = 1; p < W; ++p) v += red[slot * W + p];
+  }
+  return v;
+}
+
 // Modulation row for activation row `row` = b * L + l.
 __device__ __forceinline__ uint32_t mod_row(int32_t kind, uint32_t frames, uint32_t tpf,
                                             uint32_t row, uint32_t b, uint32_t l) {
@@ -107,42 +144,87 @@ __device__ __forceinline__ uint32_t mod_row(int32_t kind, uint32_t frames, uint3
   return b * frames + l / tpf;
 }
 
-template <bool RMS, bool FUSED, bool GATE, int AFF, int VPT>
+template <bool RMS, bool FUSED, bool GATE, int AFF, int VPT, int W, int PL, int PS>
 __global__ __launch_bounds__(kBlockThreads) void row_kernel(const RowArgs a) {
+  static_assert(W == 1 || W == 2 || W == 4, "waves per row");
+  constexpr int kRowsPerBlock = kWavesPerBlock / W;
+  [[maybe_unused]] __shared__ float red_sum[kWavesPerBlock];
+  [[maybe_unused]] __shared__ float red_sq[kWavesPerBlock];
+
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & (kWaveSize - 1);
-  const uint32_t row = blockIdx.x * kWavesPerBlock + wave;
-  if (row >= a.rows) return;  // whole wave
-
-  const uint32_t row_bytes = a.d * 2u;
-  const uint64_t row_off = (uint64_t)row * row_bytes;
-  const uint32_t b = row / a.L;
-  const uint32_t l = row - b * a.L;
-  const uint32_t srow = mod_row(a.ss_kind, a.ss_frames, a.ss_tokens_per_frame, row, b, l);
+  const uint32_t slot = wave / W;  // row slot in the workgroup
+  const uint32_t part = wave % W;  // which contiguous part of the row this wave holds
+  const uint32_t row = blockIdx.x * kRowsPerBlock + slot;
+  // With W > 1 every wave must reach the barriers, so a wave past the last
+  // row keeps going with its memory operations disabled (zero-range buffers).
+  const bool live = row < a.rows;
+  if constexpr (W == 1) {
+    if (!live) return;
+  }
+  const uint32_t row_bytes = live ? a.d * 2u : 0u;
+  const uint32_t r = live ? row : 0u;
+  const uint64_t row_off = (uint64_t)r * (a.d * 2u);
+  const uint32_t b = r / a.L;
+  const uint32_t l = r - b * a.L;
+  const uint32_t srow = mod_row(a.ss_kind, a.ss_frames, a.ss_tokens_per_frame, r, b, l);
+  // lane-local byte offset of vector v: this wave's part, then 1 KB per vector
+  const uint32_t base = (part * VPT * kWaveSize + lane) * 16u;
 
   const auto rs_x = row_rsrc((const char*)a.x + row_off, row_bytes);
   const auto rs_y = row_rsrc((const char*)a.y + row_off, row_bytes);
-  const auto rs_sc = row_rsrc((const char*)a.scale + (uint64_t)srow * row_bytes, row_bytes);
-  const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * row_bytes, row_bytes);
+  const auto rs_sc = row_rsrc((const char*)a.scale + (uint64_t)srow * (a.d * 2u), row_bytes);
+  const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * (a.d * 2u), row_bytes);
 
-  u32x4 h[VPT];   // the row, bf16-packed: residual_out (fused) or x (norm-only)
-  float sum = 0.f;
-
+  // ---- every load of the row, before any store ----
+  u32x4 h[VPT];  // x (norm-only) or residual, later the bf16-packed residual_out
+  [[maybe_unused]] u32x4 xv[VPT];
+  [[maybe_unused]] u32x4 gv[VPT];
+  [[maybe_unused]] u32x4 wv[VPT];
+  [[maybe_unused]] u32x4 bv[VPT];
+  u32x4 sc[VPT], sh[VPT];
   if constexpr (FUSED) {
     const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
-    const auto rs_ro = row_rsrc((const char*)a.residual_out + row_off, row_bytes);
-    u32x4 xv[VPT];
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream>(rs_x, (v * kWaveSize + lane) * 16u);
+    for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream>(rs_r, (v * kWaveSize + lane) * 16u);
-    u32x4 gv[VPT];
+    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_r, base + v * 1024u);
     if constexpr (GATE) {
-      const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, row, b, l);
-      const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * row_bytes, row_bytes);
+      const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, r, b, l);
+      const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * (a.d * 2u), row_bytes);
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) gv[v] = load16<kPolicyDefault>(rs_g, (v * kWaveSize + lane) * 16u);
+      for (int v = 0; v < VPT; ++v) gv[v] = load16<kPolicyDefault, PL>(rs_g, base + v * 1024u);
     }
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
+  }
+  if constexpr (AFF >= kAffWeight) {
+    const auto rs_w = row_rsrc(a.weight, row_bytes);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) wv[v] = load16<kPolicyDefault, PL>(rs_w, base + v * 1024u);
+  }
+  if constexpr (AFF >= kAffWeightBias) {
+    const auto rs_b = row_rsrc(a.bias, row_bytes);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) bv[v] = load16<kPolicyDefault, PL>(rs_b, base + v * 1024u);
+  }
+  // per-row scale/shift stream like the activations; shared rows stay cached
+  if (a.ss_kind == 1) {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) sc[v] = load16<kPolicyStream, PL>(rs_sc, base + v * 1024u);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) sh[v] = load16<kPolicyStream, PL>(rs_sh, base + v * 1024u);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) sc[v] = load16<kPolicyDefault, PL>(rs_sc, base + v * 1024u);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) sh[v] = load16<kPolicyDefault, PL>(rs_sh, base + v * 1024u);
+  }
+
+  // ---- residual update (fused) ----
+  if constexpr (FUSED) {
+    const auto rs_ro = row_rsrc((const char*)a.residual_out + row_off, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       u32x4 o;
@@ -160,12 +242,9 @@ __global__ __launch_bounds__(kBlockThreads) void row_kernel(const RowArgs a) {
         }
         o[j] = pack_bf16(s0, s1);
       }
-      store16<kPolicyStream>(o, rs_ro, (v * kWaveSize + lane) * 16u);
+      store16<kPolicyStream, PS>(o, rs_ro, base + v * 1024u);
       h[v] = o;
     }
-  } else {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream>(rs_x, (v * kWaveSize + lane) * 16u);
   }
 
   // ---- statistics (fp32) ----
@@ -173,24 +252,25 @@ __global__ __launch_bounds__(kBlockThreads) void row_kernel(const RowArgs a) {
   float mean = 0.f;
   float sq = 0.f;
   if constexpr (!RMS) {
+    float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
-    mean = wave_sum(sum) / (float)a.d;
+    mean = row_sum<W>(sum, red_sum, wave, slot) / (float)a.d;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
-      float part = 0.f;
+      float part_sq = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float d0 = lo_f32(h[v][j]) - mean;
         const float d1 = hi_f32(h[v][j]) - mean;
-        part = __builtin_fmaf(d0, d0, part);
-        part = __builtin_fmaf(d1, d1, part);
+        part_sq = __builtin_fmaf(d0, d0, part_sq);
+        part_sq = __builtin_fmaf(d1, d1, part_sq);
       }
       // lanes past the end of a ragged row hold zeros, which are not zero
       // after centring: leave them out.
-      sq += ((uint32_t)(v * kWaveSize) + lane < a.nvec) ? part : 0.f;
+      sq += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
     }
   } else {
 #pragma unroll
@@ -203,57 +283,48 @@ __global__ __launch_bounds__(kBlockThreads) void row_kernel(const RowArgs a) {
         sq = __builtin_fmaf(h1, h1, sq);
       }
   }
-  float var = wave_sum(sq) * inv_d;
+  float var = row_sum<W>(sq, red_sq, wave, slot) * inv_d;
   var = var > 0.f ? var : 0.f;
   const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
 
   // ---- epilogue from the register cache ----
-  [[maybe_unused]] __amdgpu_buffer_rsrc_t rs_w, rs_b;
-  if constexpr (AFF >= kAffWeight) rs_w = row_rsrc(a.weight, row_bytes);
-  if constexpr (AFF >= kAffWeightBias) rs_b = row_rsrc(a.bias, row_bytes);
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
-    const uint32_t off = (v * kWaveSize + lane) * 16u;
-    const u32x4 sc = load16<kPolicyDefault>(rs_sc, off);
-    const u32x4 sh = load16<kPolicyDefault>(rs_sh, off);
-    [[maybe_unused]] u32x4 wv, bv;
-    if constexpr (AFF >= kAffWeight) wv = load16<kPolicyDefault>(rs_w, off);
-    if constexpr (AFF >= kAffWeightBias) bv = load16<kPolicyDefault>(rs_b, off);
     u32x4 o;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float n0 = (lo_f32(h[v][j]) - mean) * rstd;
       float n1 = (hi_f32(h[v][j]) - mean) * rstd;
       if constexpr (AFF == kAffWeight) {
-        n0 *= lo_f32(wv[j]);
-        n1 *= hi_f32(wv[j]);
+        n0 *= lo_f32(wv[v][j]);
+        n1 *= hi_f32(wv[v][j]);
       } else if constexpr (AFF == kAffWeightBias) {
-        n0 = __builtin_fmaf(n0, lo_f32(wv[j]), lo_f32(bv[j]));
-        n1 = __builtin_fmaf(n1, hi_f32(wv[j]), hi_f32(bv[j]));
+        n0 = __builtin_fmaf(n0, lo_f32(wv[v][j]), lo_f32(bv[v][j]));
+        n1 = __builtin_fmaf(n1, hi_f32(wv[v][j]), hi_f32(bv[v][j]));
       }
-      const float t0 = __builtin_fmaf(n0, 1.0f + lo_f32(sc[j]), lo_f32(sh[j]));
-      const float t1 = __builtin_fmaf(n1, 1.0f + hi_f32(sc[j]), hi_f32(sh[j]));
+      const float t0 = __builtin_fmaf(n0, 1.0f + lo_f32(sc[v][j]), lo_f32(sh[v][j]));
+      const float t1 = __builtin_fmaf(n1, 1.0f + hi_f32(sc[v][j]), hi_f32(sh[v][j]));
       o[j] = pack_bf16(t0, t1);
     }
-    store16<kPolicyStream>(o, rs_y, off);
+    store16<kPolicyStream, PS>(o, rs_y, base + v * 1024u);
   }
 }
 
-// Table of one flag combination over every compiled register-cache width.
+// Table of one flag combination over every compiled shape.
 template <bool RMS, bool FUSED, bool GATE, int AFF>
-KernelFn kernel_for_width(int vec_index) {
-  switch (vec_index) {
+KernelFn kernel_for_shape(int shape) {
+  switch (shape) {
 #define RN_CASE(i) \
   case i:          \
-    return row_kernel<RMS, FUSED, GATE, AFF, kVecWidths[i]>;
-    RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6)
-    RN_CASE(7) RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12)
+    return row_kernel<RMS, FUSED, GATE, AFF, kShapes[i].vpt, kShapes[i].w, kPaceLoads, kPaceStores>;
+    RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
+    RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumVecWidths == 13, "kernel_for_width lists every width");
+static_assert(kNumShapes == 15, "kernel_for_shape lists every shape");
 
 }  // namespace rn

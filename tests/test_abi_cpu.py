@@ -151,14 +151,27 @@ def test_status_mapping_in_binding(rn):
 
 
 def test_describe_launch(rn):
+    """The planner: smallest waves-per-row that covers D within the register
+    budget (vectors per lane x row operands <= 52)."""
     info = rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True)
-    assert info["vec_per_lane"] == 10 and info["block_threads"] == 256
+    assert (info["waves_per_row"], info["vec_per_lane"]) == (1, 10)
+    assert info["block_threads"] == 256 and info["rows_per_block"] == 4
     assert info["grid_blocks"] == 176400 // 4
-    assert rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)["vec_per_lane"] == 20
+    c3 = rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)
+    assert (c3["waves_per_row"], c3["vec_per_lane"], c3["rows_per_block"]) == (4, 5, 1)
+    assert c3["grid_blocks"] == 90000
+    nss = rn.describe_launch(1, 176400, 5120, 0, False)
+    assert (nss["waves_per_row"], nss["vec_per_lane"]) == (1, 10)
     assert rn.describe_launch(1, 3, 8, 0, False)["vec_per_lane"] == 1
     assert rn.describe_launch(1, 3, 1000, 0, False)["vec_per_lane"] == 2
-    assert rn.describe_launch(1, 3, 16384, 0, False)["vec_per_lane"] == 32
+    big = rn.describe_launch(1, 3, 16384, 0, False)
+    assert (big["waves_per_row"], big["vec_per_lane"]) == (4, 8)
+    mid = rn.describe_launch(1, 3, 8192, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS, True)
+    assert (mid["waves_per_row"], mid["vec_per_lane"]) == (4, 4)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
+    for D in range(8, 16385, 8):
+        i = rn.describe_launch(1, 1, D, 0, False)
+        assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
     with pytest.raises(rn.RnError):
         rn.describe_launch(1, 3, 20000, 0, False)
 

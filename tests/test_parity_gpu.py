@@ -50,8 +50,10 @@ def _run_full(rn, orc, wl, check_rows=None):
     del d, y, ro
     log("workload %s: oracle on %d rows x %d threads" % (wl.name, wl.R, THREADS))
     y_ref, ro_ref, _ = orc.run_workload(wl, inp, threads=THREADS)
-    max_ulp, exact = compare_outputs(yh, y_ref, roh, ro_ref, wl.name)
-    log("workload %s: OK  y max err %.2f ulp, %.5f%% bit-identical" % (wl.name, max_ulp, 100 * exact))
+    st = compare_outputs(yh, y_ref, roh, ro_ref, wl.name)
+    log("workload %s: OK  residual_out bit-exact; y: max %.0f ulp where |y|>=1, max %.0f ulp where "
+        "|y|>=2^-6, max abs err %.3g, %.5f%% bit-identical"
+        % (wl.name, st["ulp_ge1"], st["ulp_ge_1_64"], st["abs"], 100 * st["identical"]))
     return inp, yh, roh
 
 
@@ -339,3 +341,31 @@ def test_mean_offset_rows(rn, orc):
     torch.cuda.synchronize()
     y_ref, _ = orc.nss(x, None, None, sc, sh, 1, L, D, False)
     compare_outputs(to_host(y), y_ref, what="mean offset 300")
+
+
+def _shape_cases(rn):
+    """One (D, fused, flags) per compiled (waves per row, vectors per lane) shape."""
+    seen = {}
+    flag_sets = [(False, 0), (True, rn.RN_GATE), (True, rn.RN_GATE | rn.RN_WEIGHT),
+                 (True, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS), (False, rn.RN_WEIGHT | rn.RN_BIAS)]
+    for D in range(8, 16385, 8):
+        for fused, flags in flag_sets:
+            i = rn.describe_launch(1, 1, D, flags, fused)
+            key = (i["waves_per_row"], i["vec_per_lane"])
+            if key not in seen:
+                seen[key] = (D, fused, flags)
+    return seen
+
+
+def test_every_compiled_shape(rn, orc):
+    """Every compiled (waves per row, vectors per lane) shape the planner can
+    pick, at the first row width that selects it (a ragged row for most), with
+    B=2, L=5 (so the last workgroup of a multi-row shape is partly empty)."""
+    cases = _shape_cases(rn)
+    assert len(cases) == 15, sorted(cases)
+    for (w, vpt), (D, fused, flags) in sorted(cases.items()):
+        log("shape W=%d VPT=%d via D=%d fused=%s flags=%d" % (w, vpt, D, fused, flags))
+        aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
+        gl = (FRAME, 5) if flags & rn.RN_GATE else None
+        for rms in (False, True):
+            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, (ROW, 0), 2, 5, D)
