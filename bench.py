@@ -239,7 +239,8 @@ def main():
                            "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
                            "algorithmic_bytes": wc.algorithmic_bytes(),
                            "traffic": measured_traffic(wc.name)})
-    info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused")
+    info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused",
+                              wl.gate_layout or (0, 0), wl.ss_layout)
     ref = copy_reference(args.steps, args.warmup, dev)
     log("copy reference: %.1f GB/s" % ref["GB/s"])
     line = {

@@ -123,7 +123,9 @@ const char* rn_last_error(void);
 /* Launch shape the library would use for a problem (host-only query; no
  * device work, usable without a GPU): 16-byte vectors per lane and operand,
  * waves per activation row, waves and rows per workgroup, workgroup size and
- * grid size.  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd (0). */
+ * grid size.  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
+ * (0); the layouts matter because per-row modulation operands add HBM
+ * streams, which changes the preferred shape. */
 typedef struct {
   int32_t vec_per_lane;
   int32_t waves_per_row;
@@ -134,7 +136,7 @@ typedef struct {
 } rn_launch_info;
 
 rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
-                             rn_launch_info* info);
+                             rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info);
 
 /* Library version string. */
 const char* rn_version(void);

@@ -64,7 +64,7 @@ def _load() -> ctypes.CDLL:
     lib.norm_scale_shift_fwd.restype = ctypes.c_int
     lib.rn_last_error.argtypes = []
     lib.rn_last_error.restype = ctypes.c_char_p
-    lib.rn_describe_launch.argtypes = [I64, I64, I64, U32, ctypes.c_int32,
+    lib.rn_describe_launch.argtypes = [I64, I64, I64, U32, ctypes.c_int32, rn_layout, rn_layout,
                                        ctypes.POINTER(rn_launch_info)]
     lib.rn_describe_launch.restype = ctypes.c_int
     lib.rn_version.argtypes = []
@@ -142,10 +142,12 @@ def norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
                                      _stream(stream)))
 
 
-def describe_launch(B, L, D, flags, fused=True) -> dict:
+def describe_launch(B, L, D, flags, fused=True, gate_layout=(RN_BCAST, 0),
+                    ss_layout=(RN_BCAST, 0)) -> dict:
+    """Launch shape the library picks for a problem (host-only query)."""
     info = rn_launch_info()
     _check(_lib.rn_describe_launch(int(B), int(L), int(D), int(flags), int(bool(fused)),
-                                   ctypes.byref(info)))
+                                   _layout(gate_layout), _layout(ss_layout), ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in rn_launch_info._fields_}
 
 

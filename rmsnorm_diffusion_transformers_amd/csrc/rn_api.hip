@@ -105,16 +105,27 @@ int row_operands(uint32_t flags, bool fused) {
   return n;
 }
 
-// First compiled shape that covers a row of D elements within the register
-// budget; else the widest shape that covers it; -1 if none does.
-int shape_for(int64_t D, uint32_t flags, bool fused) {
+// Tensors streamed through HBM per row: x and y, the residual pair of the
+// fused op, and per-row modulation operands.
+int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_layout) {
+  int n = 2;
+  if (fused) n += 2;
+  if (ss_layout.kind == RN_ROW) n += 2;
+  if (fused && (flags & RN_GATE) && gate_layout.kind == RN_ROW) n += 1;
+  return n;
+}
+
+// The compiled shape for a problem (see kShapes); -1 if none covers D.
+int shape_for(int64_t D, uint32_t flags, bool fused, int streams) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused);
+  const bool many = streams >= 5 && D >= rn::kManyStreamsMinD;
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
     if ((int64_t)rn::kWaveSize * s.w * s.vpt < nvec) continue;
-    if (s.vpt * ops <= rn::kVgprBudget) return i;
+    if ((s.w == 10) != many) continue;
+    if (many || s.vpt * ops <= rn::kVgprBudget) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
   return fallback;
@@ -205,7 +216,8 @@ rn_status run(const Problem& p, void* stream) {
   if (st != RN_OK) return st;
   const int64_t R = p.B * p.L;
   if (R == 0) return RN_OK;
-  const int vi = shape_for(p.D, p.flags, p.fused);
+  const int vi = shape_for(p.D, p.flags, p.fused,
+                           hbm_streams(p.flags, p.fused, p.gate_layout, p.ss_layout));
   rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
   if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
 
@@ -232,10 +244,10 @@ rn_status run(const Problem& p, void* stream) {
   a.ss_tokens_per_frame = tokens_per_frame(p.ss_layout, p.L);
   if (!(p.flags & RN_GATE)) a.gate_kind = RN_BCAST;
 
-  const int64_t rows_per_block = rn::kWavesPerBlock / rn::kShapes[vi].w;
-  const int64_t blocks = (R + rows_per_block - 1) / rows_per_block;
+  const rn::Shape shape = rn::kShapes[vi];
+  const int64_t blocks = (R + shape.rpb - 1) / shape.rpb;
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)blocks), dim3(rn::kBlockThreads), args, 0,
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)blocks), dim3(rn::kWaveSize * shape.w * shape.rpb), args, 0,
                                  (hipStream_t)stream);
   if (e != hipSuccess) return fail(RN_ELAUNCH, "hipLaunchKernel failed: %s", hipGetErrorString(e));
   return RN_OK;
@@ -265,19 +277,19 @@ rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const
 const char* rn_last_error(void) { return g_err; }
 
 rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
-                             rn_launch_info* info) {
+                             rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info) {
   g_err[0] = '\0';
   if (!info) return fail(RN_EINVAL, "info is NULL");
   rn_status st = check_shape(B, L, D, flags, fused != 0);
   if (st != RN_OK) return st;
-  const int vi = shape_for(D, flags, fused != 0);
+  const int vi = shape_for(D, flags, fused != 0, hbm_streams(flags, fused != 0, gate_layout, ss_layout));
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
   const rn::Shape s = rn::kShapes[vi];
   info->vec_per_lane = s.vpt;
   info->waves_per_row = s.w;
-  info->waves_per_block = rn::kWavesPerBlock;
-  info->rows_per_block = rn::kWavesPerBlock / s.w;
-  info->block_threads = rn::kBlockThreads;
+  info->waves_per_block = s.w * s.rpb;
+  info->rows_per_block = s.rpb;
+  info->block_threads = rn::kWaveSize * s.w * s.rpb;
   info->grid_blocks = (B * L + info->rows_per_block - 1) / info->rows_per_block;
   return RN_OK;
 }

@@ -6,23 +6,33 @@
 
 namespace rn {
 
-// A 256-thread workgroup of kWavesPerBlock waves.  W waves own one activation
-// row (W = 1, 2 or 4), so a workgroup holds kWavesPerBlock / W rows.
 constexpr int kWaveSize = 64;
-constexpr int kWavesPerBlock = 4;
-constexpr int kBlockThreads = kWaveSize * kWavesPerBlock;
 
-// Compiled shapes: (waves per row W, 16-byte vectors per lane VPT).  One wave
-// holds W-th of a row, VPT vectors of 8 bf16 per lane per operand, so a shape
+// Compiled shapes: W waves per activation row, RPB rows per workgroup (a
+// workgroup is W * RPB waves), VPT 16-byte vectors per lane.  One wave holds
+// a W-th of a row, VPT vectors of 8 bf16 per lane per operand, so a shape
 // covers rows of up to 64 * W * VPT vectors (D = 512 * W * VPT); tail lanes of
-// shorter rows are masked.  The launcher takes the first shape, in this
-// order, that covers D and keeps VPT * (row operands loaded) <= kVgprBudget.
+// shorter rows are masked.
+//
+// Choice (measured on MI355X at L = 90000-176400):
+//   * a problem that streams at most 4 tensors through HBM (x, y, and the
+//     residual pair of the fused op; broadcast / per-frame modulation rows
+//     come from L2) runs best with long per-wave rows: the first shape with
+//     W < 10, in this order, that covers D and keeps VPT * (row operands
+//     loaded) <= kVgprBudget -- one wave per row at D = 5120;
+//   * a problem that also streams per-row scale/shift (or a per-row gate)
+//     runs best with 10 waves per row and 1-4 vectors per lane (shorter
+//     per-wave spans and more rows in flight), once D >= kManyStreamsMinD.
 struct Shape {
   int w;
   int vpt;
+  int rpb;
 };
-constexpr Shape kShapes[] = {{1, 1}, {1, 2}, {1, 3}, {1, 4},  {1, 5}, {1, 6}, {1, 8}, {1, 10},
-                             {2, 6}, {2, 8}, {2, 10}, {4, 4}, {4, 5}, {4, 6}, {4, 8}};
+constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1, 5, 4},
+                             {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 6, 2},  {2, 8, 2},
+                             {2, 10, 2}, {4, 4, 1},  {4, 5, 1},  {4, 6, 1},  {4, 8, 1},
+                             {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
+constexpr int kManyStreamsMinD = 2560;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough

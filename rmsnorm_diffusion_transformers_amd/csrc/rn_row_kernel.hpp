@@ -12,9 +12,9 @@
 //   y            = bf16(n * (1 + scale) + shift)
 //
 // Design (HBM-bound; no matrix cores -- nothing here is a contraction):
-//   * W wave64s own one activation row (W = 1, 2 or 4); a 256-thread
-//     workgroup holds 4 / W rows.  Row indices are wave-uniform, so per-row
-//     quantities (descriptors, modulation row, statistics) live in SGPRs.
+//   * W wave64s own one activation row and a workgroup holds RPB rows
+//     (W * RPB waves).  Row indices are wave-uniform, so per-row quantities
+//     (descriptors, modulation row, statistics) live in SGPRs.
 //   * Every global access is a 128-bit buffer load/store (8 bf16 per lane) on
 //     a per-row buffer descriptor whose range is exactly the row: lanes past
 //     the end of a ragged row read zeros and their stores are dropped by the
@@ -144,12 +144,12 @@ __device__ __forceinline__ uint32_t mod_row(int32_t kind, uint32_t frames, uint3
   return b * frames + l / tpf;
 }
 
-template <bool RMS, bool FUSED, bool GATE, int AFF, int VPT, int W, int PL, int PS>
-__global__ __launch_bounds__(kBlockThreads) void row_kernel(const RowArgs a) {
-  static_assert(W == 1 || W == 2 || W == 4, "waves per row");
-  constexpr int kRowsPerBlock = kWavesPerBlock / W;
-  [[maybe_unused]] __shared__ float red_sum[kWavesPerBlock];
-  [[maybe_unused]] __shared__ float red_sq[kWavesPerBlock];
+template <bool RMS, bool FUSED, bool GATE, int AFF, int VPT, int W, int RPB, int PL, int PS>
+__global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs a) {
+  static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
+  constexpr int kRowsPerBlock = RPB;
+  [[maybe_unused]] __shared__ float red_sum[W * RPB];
+  [[maybe_unused]] __shared__ float red_sq[W * RPB];
 
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & (kWaveSize - 1);
@@ -316,15 +316,17 @@ KernelFn kernel_for_shape(int shape) {
   switch (shape) {
 #define RN_CASE(i) \
   case i:          \
-    return row_kernel<RMS, FUSED, GATE, AFF, kShapes[i].vpt, kShapes[i].w, kPaceLoads, kPaceStores>;
+    return row_kernel<RMS, FUSED, GATE, AFF, kShapes[i].vpt, kShapes[i].w, kShapes[i].rpb, \
+                      kPaceLoads, kPaceStores>;
     RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
     RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
+    RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumShapes == 15, "kernel_for_shape lists every shape");
+static_assert(kNumShapes == 19, "kernel_for_shape lists every shape");
 
 }  // namespace rn

@@ -157,9 +157,16 @@ def test_describe_launch(rn):
     assert (info["waves_per_row"], info["vec_per_lane"]) == (1, 10)
     assert info["block_threads"] == 256 and info["rows_per_block"] == 4
     assert info["grid_blocks"] == 176400 // 4
-    c3 = rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)
-    assert (c3["waves_per_row"], c3["vec_per_lane"], c3["rows_per_block"]) == (4, 5, 1)
-    assert c3["grid_blocks"] == 90000
+    c3 = rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT, True,
+                            (rn.RN_BCAST, 0), (rn.RN_ROW, 0))
+    assert (c3["waves_per_row"], c3["vec_per_lane"], c3["rows_per_block"]) == (10, 2, 1)
+    assert c3["grid_blocks"] == 90000 and c3["block_threads"] == 640
+    c3b = rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)
+    assert (c3b["waves_per_row"], c3b["vec_per_lane"], c3b["rows_per_block"]) == (4, 5, 1)
+    c5 = rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True, (rn.RN_FRAME, 49), (rn.RN_FRAME, 49))
+    assert (c5["waves_per_row"], c5["vec_per_lane"]) == (1, 10)
+    small_row = rn.describe_launch(1, 8, 1024, rn.RN_GATE, True, (rn.RN_ROW, 0), (rn.RN_ROW, 0))
+    assert small_row["waves_per_row"] == 1
     nss = rn.describe_launch(1, 176400, 5120, 0, False)
     assert (nss["waves_per_row"], nss["vec_per_lane"]) == (1, 10)
     assert rn.describe_launch(1, 3, 8, 0, False)["vec_per_lane"] == 1
@@ -170,8 +177,10 @@ def test_describe_launch(rn):
     assert (mid["waves_per_row"], mid["vec_per_lane"]) == (4, 4)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
     for D in range(8, 16385, 8):
-        i = rn.describe_launch(1, 1, D, 0, False)
-        assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
+        for fused, flags, gl, sl in ((False, 0, (0, 0), (0, 0)), (True, 14, (1, 0), (1, 0))):
+            i = rn.describe_launch(1, 1, D, flags, fused, gl, sl)
+            assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
+            assert i["block_threads"] == 64 * i["waves_per_block"] <= 1024
     with pytest.raises(rn.RnError):
         rn.describe_launch(1, 3, 20000, 0, False)
 
