@@ -437,6 +437,144 @@ def pin_invariants(o, seed: int = 10):
         assert np.all(np.abs(np.sqrt((t * t).mean(1))[keep] - 1) <= 1e-3)
 
 
-FAST_PINS = [pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
+# --------------------------------------------------------------------------- extensions
+
+def _torch_e4m3(f32: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+E4M3_VALUES = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(
+    torch.float64).numpy()   # decode table (index = code), from torch
+
+
+def pin_e4m3_vs_torch(o, stride: int = 1, threads: int = 8):
+    """binary64 -> FP8 E4M3 (nearest, ties to even) equals torch's float32 ->
+    float8_e4m3fn cast on every binary32 value with |x| < 464 (the inputs torch
+    rounds to a finite value); larger magnitudes saturate to +-448; NaN -> 0x7F."""
+    from concurrent.futures import ThreadPoolExecutor
+    limit = int(np.array([464.0], np.float32).view(np.uint32)[0])
+    chunk = 1 << 25
+    starts = list(range(0, limit, chunk * stride if stride > 1 else chunk))
+
+    def one(s0):
+        if stride == 1:
+            mag = np.arange(s0, min(limit, s0 + chunk), dtype=np.uint64).astype(np.uint32)
+        else:
+            mag = np.arange(s0, min(limit, s0 + chunk * stride), stride, dtype=np.uint64).astype(np.uint32)
+        for sign in (0, 0x80000000):
+            f = (mag | np.uint32(sign)).view(np.float32)
+            got = o.f64_to_e4m3(f.astype(np.float64))
+            ref = _torch_e4m3(f)
+            bad = got != ref
+            if bad.any():
+                i = int(np.argmax(bad))
+                return "f32 %r: oracle %02x torch %02x" % (float(f[i]), got[i], ref[i])
+        return None
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for msg in ex.map(one, starts):
+            assert msg is None, msg
+    sat = o.f64_to_e4m3(np.array([464.0, 464.00001, 479.9, 480.0, 1e30, np.inf, -500.0, -np.inf]))
+    assert sat.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE], sat
+    assert o.f64_to_e4m3(np.array([np.nan]))[0] == 0x7F
+    # values between binary32 neighbours: the table-nearest rule on binary64 inputs
+    rng = np.random.default_rng(12)
+    t = rng.standard_normal(100000) * np.exp2(rng.integers(-12, 9, 100000).astype(np.float64))
+    t = t[np.abs(t) < 460]
+    got = o.f64_to_e4m3(t)
+    fin = np.arange(0, 127)               # +0 .. 448
+    vals = E4M3_VALUES[fin]
+    a = np.abs(t)
+    hi = np.clip(np.searchsorted(vals, a), 1, 126)
+    lo = hi - 1
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where((dhi < dlo) | ((dhi == dlo) & (fin[hi] % 2 == 0)), fin[hi], fin[lo])
+    pick = pick | np.where(np.signbit(t), 0x80, 0)
+    assert np.array_equal(got, pick.astype(np.uint8))
+
+
+def pin_affine_f32(o, seed: int = 13):
+    """binary32 weight/bias are used at full precision: with scale = shift = 0
+    the oracle equals torch layer_norm / rms_norm in float64 with the float32
+    weights widened exactly, to 1e-12; weights that are not bf16 values change
+    the result relative to their bf16 rounding."""
+    F = torch.nn.functional
+    rng = np.random.default_rng(seed)
+    for D in (64, 1000, 5120):
+        x = synth.random_bf16((6, D), seed + D, 1)
+        w = (1.0 + 0.05 * rng.standard_normal(D)).astype(np.float32)
+        b = (0.1 * rng.standard_normal(D)).astype(np.float32)
+        xt = torch.from_numpy(bf16_to_f64(x))
+        eps = float(np.float32(1e-6))
+        z = _zeros(1, D)
+        _, t = o.nss(x, w, b, z, z, 1, 6, D, False, want_t=True, affine_f32=True)
+        ref = F.layer_norm(xt, (D,), weight=torch.from_numpy(w.astype(np.float64)),
+                           bias=torch.from_numpy(b.astype(np.float64)), eps=eps)
+        np.testing.assert_allclose(t, ref.numpy(), rtol=1e-12, atol=1e-12)
+        _, t = o.nss(x, w, None, z, z, 1, 6, D, True, want_t=True, affine_f32=True)
+        ref = F.rms_norm(xt, (D,), weight=torch.from_numpy(w.astype(np.float64)), eps=eps)
+        np.testing.assert_allclose(t, ref.numpy(), rtol=1e-12, atol=1e-12)
+        wb = (w.view(np.uint32) >> 16).astype(np.uint16)   # a bf16 version of w
+        _, t16 = o.nss(x, wb, None, z, z, 1, 6, D, True, want_t=True)
+        assert not np.array_equal(t, t16)
+
+
+def pin_y_f32(o, seed: int = 14):
+    """The binary32 output is the nearest-even binary32 value of t (numpy's
+    IEEE cast), for both ops."""
+    D, L = 320, 12
+    x = synth.random_bf16((L, D), seed, 1)
+    r = synth.random_bf16((L, D), seed, 2)
+    g = synth.random_bf16((1, D), seed, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
+    sc = synth.random_bf16((1, D), seed, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), seed, 7, a=0.0, b=0.1)
+    for rms in (False, True):
+        y, t = o.nss(x, None, None, sc, sh, 1, L, D, rms, want_t=True, y_dtype=1)
+        assert y.dtype == np.float32 and np.array_equal(y, t.astype(np.float32))
+        y, ro, t = o.fused(x, r, g, None, None, sc, sh, 1, L, D, rms, want_t=True, y_dtype=1)
+        assert np.array_equal(y, t.astype(np.float32))
+        y16, ro16, _ = o.fused(x, r, g, None, None, sc, sh, 1, L, D, rms)
+        assert np.array_equal(ro, ro16)
+
+
+def pin_fp8_rows(o, seed: int = 15):
+    """FP8 output: per-row scale s = max|t| / 448 (binary32) and codes E4M3(t / s).
+    With scale = -1 the row is t = shift exactly: a shift row whose largest
+    magnitude is 448 gives s = 1 and codes equal to torch's cast of the shift
+    values.  Random rows: s is the binary32 rounding of max|t| / 448; the
+    largest code decodes to +-448; every element decodes to t within half an
+    E4M3 step (2^-4 relative, or s * 2^-10 for subnormals); an all-zero row gives
+    s = 0 and zero codes."""
+    D = 16
+    vals = np.array([448, -3.5, 0.25, 1.0625, 1.1875, -0.001953125, 0, 100, -448, 2 ** -7,
+                     13, -17, 0.5, 7.5, 240, -0.75])
+    sh = _bits(vals)[None, :]
+    x = synth.random_bf16((2, D), seed, 1)
+    y, t, s = o.nss(x, None, None, _const(1, D, -1.0), sh, 1, 2, D, False, want_t=True, y_dtype=2)
+    assert s.tolist() == [1.0, 1.0]
+    ref = _torch_e4m3(bf16_to_f32(sh[0]))
+    assert np.array_equal(y[0], ref) and np.array_equal(y[1], ref)
+    # random rows
+    L, D = 40, 1000
+    x = synth.random_bf16((L, D), seed, 1)
+    sc = synth.random_bf16((1, D), seed, 6, a=0.0, b=0.1)
+    shr = synth.random_bf16((1, D), seed, 7, a=0.0, b=0.1)
+    for rms in (False, True):
+        y, t, s = o.nss(x, None, None, sc, shr, 1, L, D, rms, want_t=True, y_dtype=2)
+        amax = np.abs(t).max(1)
+        assert np.array_equal(s, (amax / 448.0).astype(np.float32))
+        dec = E4M3_VALUES[y]
+        assert np.all(np.abs(dec).max(1) == 448.0)
+        err = np.abs(dec * s[:, None].astype(np.float64) - t)
+        bound = 2.0 ** -4 * np.abs(t) + s[:, None] * 2.0 ** -10
+        assert np.all(err <= bound * (1 + 1e-9))
+    z = _zeros(3, D)
+    y, _, s = o.nss(z, None, None, _zeros(1, D), _zeros(1, D), 1, 3, D, False, want_t=True,
+                    y_dtype=2)
+    assert np.all(s == 0) and np.all(y == 0)
+
+
+FAST_PINS = [pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
              pin_torch_norms, pin_layouts, pin_fused_is_nss_of_residual, pin_scale_invariance,
              pin_random_rows_ld, pin_invariants]

@@ -32,8 +32,8 @@ MUTANTS = {
     "eps_dropped": ("double rho = 1.0 / sqrt(var + eps);", "double rho = 1.0 / sqrt(var);"),
     "rms_centred": ("if (!is_rms) {", "if (1) {"),
     "mean_not_subtracted": ("double n = (h[c] - mean) * rho;", "double n = h[c] * rho;"),
-    "bias_before_weight": ("    if (w) n = n * orc_bf16_to_f64(w[c]);\n    if (bias) n = n + orc_bf16_to_f64(bias[c]);",
-                           "    if (bias) n = n + orc_bf16_to_f64(bias[c]);\n    if (w) n = n * orc_bf16_to_f64(w[c]);"),
+    "bias_before_weight": ("    if (w) n = n * operand(w, affine_f32, c);\n    if (bias) n = n + operand(bias, affine_f32, c);",
+                           "    if (bias) n = n + operand(bias, affine_f32, c);\n    if (w) n = n * operand(w, affine_f32, c);"),
     "frame_index_modulo": ("return b * frames + l / (L / frames);", "return b * frames + l % frames;"),
     "frame_ignores_batch": ("return b * frames + l / (L / frames);", "return l / (L / frames);"),
     "bcast_per_batch": ("case ORC_BCAST: return 0;", "case ORC_BCAST: return b;"),
@@ -41,6 +41,16 @@ MUTANTS = {
     "round_toward_zero": ("double r = rint(a / q) * q;", "double r = trunc(a / q) * q;"),
     "no_subnormal_quantum": ("if (e < -126) e = -126;", ""),
     "flush_subnormals": ("if (a == 0.0) return sign;", "if (a < 0x1.0p-126) return sign;"),
+    "fp8_scale_480": ("float s = (float)(amax / 448.0);", "float s = (float)(amax / 480.0);"),
+    "fp8_not_scaled": ("orc_f64_to_e4m3(t[c] / (double)s)", "orc_f64_to_e4m3(t[c])"),
+    "e4m3_ties_away": ("double r = isinf(a) ? 512.0 : rint(a / q) * q;",
+                       "double r = isinf(a) ? 512.0 : round(a / q) * q;"),
+    "e4m3_exponent_bias": ("int exp_field = (er - 1) + 7;", "int exp_field = (er - 1) + 8;"),
+    "e4m3_no_saturation": ("if (r > 448.0) r = 448.0;", ""),
+    "affine_f32_read_as_bf16": ("return f32 ? (double)((const float*)p)[c] : orc_bf16_to_f64(((const uint16_t*)p)[c]);",
+                                "return orc_bf16_to_f64(((const uint16_t*)p)[c]);"),
+    "y_f32_via_bf16": ("((float*)y_row)[c] = (float)t[c];",
+                       "((float*)y_row)[c] = (float)orc_bf16_to_f64(orc_f64_to_bf16(t[c]));"),
     "gate_row_from_ss_layout": ("const uint16_t* g_row = gate ? gate + orc_mod_row(gate_kind, gate_frames, r, L) * D : NULL;",
                                 "const uint16_t* g_row = gate ? gate + orc_mod_row(ss_kind, ss_frames, r, L) * D : NULL;"),
 }
@@ -52,6 +62,7 @@ def _run_pins(o):
         lambda o: pins.pin_residual_vs_torch(o, n_res=16, n_gate=6),
         lambda o: pins.pin_round_f32_vs_torch(o, stride=65521, threads=4),
         lambda o: pins.pin_bruteforce_d8(o, stride=97, threads=4),
+        lambda o: pins.pin_e4m3_vs_torch(o, stride=4099, threads=4),
     ]
     for pin in checks:
         try:

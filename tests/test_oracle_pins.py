@@ -55,3 +55,19 @@ def test_random_rows_extended_precision(orc):
 
 def test_norm_invariants(orc):
     pins.pin_invariants(orc)
+
+
+def test_e4m3_vs_torch(orc):
+    pins.pin_e4m3_vs_torch(orc)
+
+
+def test_affine_f32(orc):
+    pins.pin_affine_f32(orc)
+
+
+def test_y_f32(orc):
+    pins.pin_y_f32(orc)
+
+
+def test_fp8_rows(orc):
+    pins.pin_fp8_rows(orc)
