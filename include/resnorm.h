@@ -69,6 +69,22 @@ typedef struct {
 /* Largest supported row width. */
 #define RN_D_MAX 16384
 
+/* Element types for rn_ext. */
+enum {
+  RN_DTYPE_BF16 = 0,      /* bfloat16 */
+  RN_DTYPE_F32 = 1,       /* IEEE binary32 */
+  RN_DTYPE_FP8_E4M3 = 2   /* OCP FP8 E4M3 ("e4m3fn"): max 448, no infinities */
+};
+
+/* Optional element types of the *_ex entry points (a NULL rn_ext pointer
+ * means all bf16). */
+typedef struct {
+  int32_t affine_dtype;  /* weight and bias: RN_DTYPE_BF16 or RN_DTYPE_F32 */
+  int32_t y_dtype;       /* y: RN_DTYPE_BF16, RN_DTYPE_F32 or RN_DTYPE_FP8_E4M3 */
+  void* y_scale;         /* RN_DTYPE_FP8_E4M3 only (else NULL): [B*L] binary32 per-row
+                            scales written by the call, y = y_scale[r] * e4m3 */
+} rn_ext;
+
 /*
  * resnorm_fused_fwd -- gated residual update + norm + modulation.
  *
@@ -115,6 +131,34 @@ rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const
                                const void* scale, const void* shift, int64_t B, int64_t L,
                                int64_t D, uint32_t flags, rn_layout ss_layout, float eps,
                                void* stream);
+
+/*
+ * resnorm_fused_fwd_ex / norm_scale_shift_fwd_ex -- the same operations with
+ * other element types (rn_ext; NULL = all bf16):
+ *   - binary32 weight / bias, used at full precision (the pages' fused-affine
+ *     call passes fp32 affine parameters: sglang PR #36349, "Microbenchmark";
+ *     the prior-art kernel casts them to bf16: sglang PR #33144, "Known gaps");
+ *   - binary32 y: the binary32 result before the final rounding, rounded to
+ *     nearest even (the pages note the two ops treat their output dtype
+ *     differently: sglang PR #33144, "Known gaps");
+ *   - FP8 E4M3 y with a per-row scale, for an FP8 consumer (the pages' WAN2.2
+ *     runs enable FP8 attention: sglang PR #36349, "Command"): for each row,
+ *     y_scale[r] = max_c |t[r,c]| / 448 and y[r,c] = E4M3(t[r,c] / y_scale[r]),
+ *     nearest even (0 for an all-zero row).  y is then [B*L, D] bytes.
+ * residual_out is bf16 in every case.  Errors as above, plus RN_EINVAL for an
+ * unknown dtype, a y_scale that is missing for FP8 (or given otherwise) or
+ * not 4-byte aligned, and overlaps of y_scale with any operand.
+ */
+rn_status resnorm_fused_fwd_ex(void* y, void* residual_out, const void* x, const void* residual,
+                               const void* gate, const void* weight, const void* bias,
+                               const void* scale, const void* shift, int64_t B, int64_t L,
+                               int64_t D, uint32_t flags, rn_layout gate_layout,
+                               rn_layout ss_layout, float eps, const rn_ext* ext, void* stream);
+
+rn_status norm_scale_shift_fwd_ex(void* y, const void* x, const void* weight, const void* bias,
+                                  const void* scale, const void* shift, int64_t B, int64_t L,
+                                  int64_t D, uint32_t flags, rn_layout ss_layout, float eps,
+                                  const rn_ext* ext, void* stream);
 
 /* Text describing the last non-OK status returned on the calling thread
  * (empty if none).  The pointer stays valid until the thread's next call. */

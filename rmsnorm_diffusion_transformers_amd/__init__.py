@@ -13,6 +13,8 @@ Low level (same names and argument order as the C entry points):
                       shift, B, L, D, flags, gate_layout, ss_layout, eps, stream)
     norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
                          ss_layout, eps, stream)
+    resnorm_fused_fwd_ex / norm_scale_shift_fwd_ex: the same plus affine_dtype,
+    y_dtype and y_scale (binary32 weight/bias; binary32 or FP8 E4M3 y)
 Tensor level (operand order of the custom ops flydsl_fused_residual_norm_scale_shift
 and flydsl_norm_scale_shift, sglang PR #36349, "Microbenchmark"):
     fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
@@ -30,12 +32,18 @@ LIB_PATH = os.path.join(_HERE, "librnorm.so")
 RN_OK, RN_EINVAL, RN_EUNSUPPORTED, RN_ELAUNCH = 0, 1, 2, 3
 RN_RMS, RN_GATE, RN_WEIGHT, RN_BIAS = 1, 2, 4, 8
 RN_BCAST, RN_ROW, RN_FRAME = 0, 1, 2
+RN_DTYPE_BF16, RN_DTYPE_F32, RN_DTYPE_FP8_E4M3 = 0, 1, 2
 RN_D_MAX = 16384
 _STATUS = {0: "RN_OK", 1: "RN_EINVAL", 2: "RN_EUNSUPPORTED", 3: "RN_ELAUNCH"}
 
 
 class rn_layout(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("frames", ctypes.c_int32)]
+
+
+class rn_ext(ctypes.Structure):
+    _fields_ = [("affine_dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
+                ("y_scale", ctypes.c_void_p)]
 
 
 class rn_launch_info(ctypes.Structure):
@@ -62,6 +70,12 @@ def _load() -> ctypes.CDLL:
     lib.resnorm_fused_fwd.restype = ctypes.c_int
     lib.norm_scale_shift_fwd.argtypes = [P, P, P, P, P, P, I64, I64, I64, U32, rn_layout, F32, P]
     lib.norm_scale_shift_fwd.restype = ctypes.c_int
+    lib.resnorm_fused_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, U32,
+                                         rn_layout, rn_layout, F32, ctypes.POINTER(rn_ext), P]
+    lib.resnorm_fused_fwd_ex.restype = ctypes.c_int
+    lib.norm_scale_shift_fwd_ex.argtypes = [P, P, P, P, P, P, I64, I64, I64, U32, rn_layout, F32,
+                                            ctypes.POINTER(rn_ext), P]
+    lib.norm_scale_shift_fwd_ex.restype = ctypes.c_int
     lib.rn_last_error.argtypes = []
     lib.rn_last_error.restype = ctypes.c_char_p
     lib.rn_describe_launch.argtypes = [I64, I64, I64, U32, ctypes.c_int32, rn_layout, rn_layout,
@@ -88,8 +102,13 @@ def _check(status: int):
         raise RnError(status, last_error())
 
 
-def _addr(t):
-    """Device address of a bf16 CUDA tensor (or an int address, or None)."""
+_DTYPE_NAMES = {RN_DTYPE_BF16: "bfloat16", RN_DTYPE_F32: "float32",
+                RN_DTYPE_FP8_E4M3: "float8_e4m3fn"}
+
+
+def _addr(t, dtype=RN_DTYPE_BF16):
+    """Device address of a contiguous CUDA tensor of the given element type
+    (or an int address, or None)."""
     if t is None:
         return None
     if isinstance(t, int):
@@ -99,11 +118,23 @@ def _addr(t):
         raise TypeError("expected a torch.Tensor, an int address or None, got %r" % type(t))
     if t.device.type != "cuda":
         raise ValueError("tensor must be on a GPU device (got %s); there is no CPU path" % t.device)
-    if t.dtype != torch.bfloat16:
-        raise TypeError("tensor must be bfloat16 (got %s)" % t.dtype)
+    want = getattr(torch, _DTYPE_NAMES[dtype])
+    if t.dtype != want:
+        raise TypeError("tensor must be %s (got %s)" % (want, t.dtype))
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr()
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt is None or dt == torch.bfloat16:
+        return RN_DTYPE_BF16
+    if dt == torch.float32:
+        return RN_DTYPE_F32
+    if dt == torch.float8_e4m3fn:
+        return RN_DTYPE_FP8_E4M3
+    raise TypeError("unsupported element type %s" % dt)
 
 
 def _stream(stream):
@@ -140,6 +171,34 @@ def norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
                                      _addr(scale), _addr(shift), int(B), int(L), int(D),
                                      int(flags), _layout(ss_layout), float(eps),
                                      _stream(stream)))
+
+
+def resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L,
+                         D, flags, gate_layout=(RN_BCAST, 0), ss_layout=(RN_BCAST, 0), eps=1e-6,
+                         affine_dtype=RN_DTYPE_BF16, y_dtype=RN_DTYPE_BF16, y_scale=None,
+                         stream=None) -> None:
+    """Enqueue the fused op with other element types (C entry point of the same
+    name): binary32 weight/bias; binary32 or FP8 E4M3 y (FP8 with per-row
+    binary32 scales in y_scale)."""
+    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    _check(_lib.resnorm_fused_fwd_ex(_addr(y, y_dtype), _addr(residual_out), _addr(x),
+                                     _addr(residual), _addr(gate),
+                                     _addr(weight, affine_dtype), _addr(bias, affine_dtype),
+                                     _addr(scale), _addr(shift), int(B), int(L), int(D),
+                                     int(flags), _layout(gate_layout), _layout(ss_layout),
+                                     float(eps), ctypes.byref(ext), _stream(stream)))
+
+
+def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
+                            ss_layout=(RN_BCAST, 0), eps=1e-6, affine_dtype=RN_DTYPE_BF16,
+                            y_dtype=RN_DTYPE_BF16, y_scale=None, stream=None) -> None:
+    """Enqueue the norm-only op with other element types (C entry point of the
+    same name)."""
+    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    _check(_lib.norm_scale_shift_fwd_ex(_addr(y, y_dtype), _addr(x), _addr(weight, affine_dtype),
+                                        _addr(bias, affine_dtype), _addr(scale), _addr(shift),
+                                        int(B), int(L), int(D), int(flags), _layout(ss_layout),
+                                        float(eps), ctypes.byref(ext), _stream(stream)))
 
 
 def describe_launch(B, L, D, flags, fused=True, gate_layout=(RN_BCAST, 0),
@@ -183,11 +242,28 @@ def _bld(x):
     raise ValueError("activations must be [B, L, D] or [L, D] (got %s)" % (tuple(x.shape),))
 
 
+def _affine_dtype(weight, bias) -> int:
+    dts = {_dtype_code(t.dtype) for t in (weight, bias) if t is not None}
+    if len(dts) > 1:
+        raise TypeError("weight and bias must have the same element type")
+    d = dts.pop() if dts else RN_DTYPE_BF16
+    if d not in (RN_DTYPE_BF16, RN_DTYPE_F32):
+        raise TypeError("weight and bias must be bfloat16 or float32")
+    return d
+
+
+def _new_y(x, y_dtype):
+    import torch
+    return torch.empty(x.shape, dtype=getattr(torch, _DTYPE_NAMES[y_dtype]), device=x.device)
+
+
 def fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
                                     norm_type: str = "layer", eps: float = 1e-6, *, y=None,
-                                    residual_out=None, stream=None):
+                                    residual_out=None, out_dtype=None, stream=None):
     """residual_out = residual + gate * x; y = norm(residual_out) [* weight + bias]
-    * (1 + scale) + shift.  Returns (y, residual_out), both bf16 like x."""
+    * (1 + scale) + shift.  weight/bias may be bfloat16 or float32; y is
+    bfloat16 (default), float32, or float8_e4m3fn (out_dtype).  Returns
+    (y, residual_out), or (y, residual_out, y_scale) for float8_e4m3fn."""
     import torch
     B, L, D = _bld(x)
     flags = _norm_flag(norm_type)
@@ -197,22 +273,28 @@ def fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shif
         flags |= RN_WEIGHT
     if bias is not None:
         flags |= RN_BIAS
+    yd = _dtype_code(out_dtype)
     if y is None:
-        y = torch.empty_like(x)
+        y = _new_y(x, yd)
     if residual_out is None:
         residual_out = torch.empty_like(residual)
+    y_scale = torch.empty((B * L,), dtype=torch.float32, device=x.device) \
+        if yd == RN_DTYPE_FP8_E4M3 else None
     gl = infer_layout(gate, B, L, D) if gate is not None else (RN_BCAST, 0)
     sl = infer_layout(scale, B, L, D)
     if infer_layout(shift, B, L, D) != sl:
         raise ValueError("scale and shift must share one layout")
-    resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
-                      flags, gl, sl, eps, stream)
+    resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                         flags, gl, sl, eps, _affine_dtype(weight, bias), yd, y_scale, stream)
+    if y_scale is not None:
+        return y, residual_out, y_scale
     return y, residual_out
 
 
 def norm_scale_shift(x, weight, bias, scale, shift, norm_type: str = "layer", eps: float = 1e-6,
-                     *, y=None, stream=None):
-    """y = norm(x) [* weight + bias] * (1 + scale) + shift (bf16 like x)."""
+                     *, y=None, out_dtype=None, stream=None):
+    """y = norm(x) [* weight + bias] * (1 + scale) + shift.  Returns y, or
+    (y, y_scale) for out_dtype float8_e4m3fn."""
     import torch
     B, L, D = _bld(x)
     flags = _norm_flag(norm_type)
@@ -220,10 +302,16 @@ def norm_scale_shift(x, weight, bias, scale, shift, norm_type: str = "layer", ep
         flags |= RN_WEIGHT
     if bias is not None:
         flags |= RN_BIAS
+    yd = _dtype_code(out_dtype)
     if y is None:
-        y = torch.empty_like(x)
+        y = _new_y(x, yd)
+    y_scale = torch.empty((B * L,), dtype=torch.float32, device=x.device) \
+        if yd == RN_DTYPE_FP8_E4M3 else None
     sl = infer_layout(scale, B, L, D)
     if infer_layout(shift, B, L, D) != sl:
         raise ValueError("scale and shift must share one layout")
-    norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags, sl, eps, stream)
+    norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags, sl, eps,
+                            _affine_dtype(weight, bias), yd, y_scale, stream)
+    if y_scale is not None:
+        return y, y_scale
     return y

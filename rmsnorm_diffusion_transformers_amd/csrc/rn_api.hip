@@ -68,6 +68,9 @@ rn_status check_layout(const char* what, rn_layout lay, int64_t L) {
 
 struct Problem {
   bool fused;
+  int affine_dtype;  // RN_DTYPE_BF16 or RN_DTYPE_F32
+  int y_dtype;       // RN_DTYPE_BF16, RN_DTYPE_F32 or RN_DTYPE_FP8_E4M3
+  float* y_scale;
   void* y;
   void* residual_out;
   const void* x;
@@ -96,12 +99,14 @@ rn_status check_shape(int64_t B, int64_t L, int64_t D, uint32_t flags, bool fuse
   return RN_OK;
 }
 
-// Row operands a kernel loads per row (each VPT vectors per lane).
-int row_operands(uint32_t flags, bool fused) {
+// Row operands a kernel holds per row, in units of VPT 16-byte vectors per
+// lane (a binary32 weight or bias counts twice).
+int row_operands(uint32_t flags, bool fused, int affine_dtype) {
+  const int aff = affine_dtype == RN_DTYPE_F32 ? 2 : 1;
   int n = 3;  // x, scale, shift
   if (fused) n += 1 + ((flags & RN_GATE) ? 1 : 0);
-  if (flags & RN_WEIGHT) n += 1;
-  if (flags & RN_BIAS) n += 1;
+  if (flags & RN_WEIGHT) n += aff;
+  if (flags & RN_BIAS) n += aff;
   return n;
 }
 
@@ -116,9 +121,9 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
 }
 
 // The compiled shape for a problem (see kShapes); -1 if none covers D.
-int shape_for(int64_t D, uint32_t flags, bool fused, int streams) {
+int shape_for(int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
   const int64_t nvec = D / 8;
-  const int ops = row_operands(flags, fused);
+  const int ops = row_operands(flags, fused, affine_dtype);
   const bool many = streams >= 5 && D >= rn::kManyStreamsMinD;
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
@@ -151,6 +156,13 @@ rn_status validate(const Problem& p) {
   if (want_b != (p.bias != nullptr))
     return fail(RN_EINVAL, want_b ? "RN_BIAS set but bias is NULL" : "bias given but RN_BIAS not set");
   if (!std::isfinite(p.eps) || p.eps < 0.f) return fail(RN_EINVAL, "eps must be finite and >= 0 (got %g)", (double)p.eps);
+  if (p.affine_dtype != RN_DTYPE_BF16 && p.affine_dtype != RN_DTYPE_F32)
+    return fail(RN_EINVAL, "affine_dtype %d is not RN_DTYPE_BF16 or RN_DTYPE_F32", p.affine_dtype);
+  if (p.y_dtype != RN_DTYPE_BF16 && p.y_dtype != RN_DTYPE_F32 && p.y_dtype != RN_DTYPE_FP8_E4M3)
+    return fail(RN_EINVAL, "y_dtype %d is not RN_DTYPE_BF16, RN_DTYPE_F32 or RN_DTYPE_FP8_E4M3", p.y_dtype);
+  if ((p.y_dtype == RN_DTYPE_FP8_E4M3) != (p.y_scale != nullptr))
+    return fail(RN_EINVAL, p.y_scale ? "y_scale given but y_dtype is not RN_DTYPE_FP8_E4M3"
+                                     : "RN_DTYPE_FP8_E4M3 output needs y_scale");
 
   if (p.fused && want_gate && (st = check_layout("gate", p.gate_layout, p.L)) != RN_OK) return st;
   if ((st = check_layout("scale/shift", p.ss_layout, p.L)) != RN_OK) return st;
@@ -159,26 +171,30 @@ rn_status validate(const Problem& p) {
   const char* names[] = {"y", "residual_out", "x", "residual", "gate", "weight", "bias", "scale", "shift"};
   for (int i = 0; i < 9; ++i)
     if (ptrs[i] && !aligned16(ptrs[i])) return fail(RN_EINVAL, "%s is not 16-byte aligned", names[i]);
+  if (p.y_scale && ((uintptr_t)p.y_scale & 3u)) return fail(RN_EINVAL, "y_scale is not 4-byte aligned");
 
-  // Overlap: outputs against every other operand; only exact y == x and
-  // residual_out == residual are allowed.
+  // Overlap: outputs against every other operand; only exact y == x (bf16 y)
+  // and residual_out == residual are allowed.
   const int64_t R = p.B * p.L;
   const uint64_t row = (uint64_t)p.D * 2u;
-  Extent ext[9];
+  const uint64_t y_row = (uint64_t)p.D * (p.y_dtype == RN_DTYPE_F32 ? 4u : p.y_dtype == RN_DTYPE_FP8_E4M3 ? 1u : 2u);
+  const uint64_t aff_row = (uint64_t)p.D * (p.affine_dtype == RN_DTYPE_F32 ? 4u : 2u);
+  Extent ext[10];
   int n = 0;
-  auto add = [&](const char* name, const void* ptr, int64_t rows, bool output) {
+  auto add = [&](const char* name, const void* ptr, int64_t rows, uint64_t row_bytes, bool output) {
     if (ptr && rows > 0)
-      ext[n++] = Extent{name, (uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)(rows * row), output};
+      ext[n++] = Extent{name, (uintptr_t)ptr, (uintptr_t)ptr + (uintptr_t)(rows * row_bytes), output};
   };
-  add("y", p.y, R, true);
-  if (p.fused) add("residual_out", p.residual_out, R, true);
-  add("x", p.x, R, false);
-  if (p.fused) add("residual", p.residual, R, false);
-  if (p.fused && want_gate) add("gate", p.gate, layout_rows(p.gate_layout, p.B, p.L), false);
-  add("weight", p.weight, 1, false);
-  add("bias", p.bias, 1, false);
-  add("scale", p.scale, layout_rows(p.ss_layout, p.B, p.L), false);
-  add("shift", p.shift, layout_rows(p.ss_layout, p.B, p.L), false);
+  add("y", p.y, R, y_row, true);
+  if (p.fused) add("residual_out", p.residual_out, R, row, true);
+  add("y_scale", p.y_scale, R, 4, true);
+  add("x", p.x, R, row, false);
+  if (p.fused) add("residual", p.residual, R, row, false);
+  if (p.fused && want_gate) add("gate", p.gate, layout_rows(p.gate_layout, p.B, p.L), row, false);
+  add("weight", p.weight, 1, aff_row, false);
+  add("bias", p.bias, 1, aff_row, false);
+  add("scale", p.scale, layout_rows(p.ss_layout, p.B, p.L), row, false);
+  add("shift", p.shift, layout_rows(p.ss_layout, p.B, p.L), row, false);
   // Inputs may share memory with each other (they are only read).
   for (int i = 0; i < n; ++i) {
     if (!ext[i].output) continue;
@@ -197,13 +213,16 @@ rn_status validate(const Problem& p) {
 }
 
 rn::KernelFn pick_kernel(const Problem& p, int vi) {
-  const int aff = (p.flags & RN_BIAS) ? rn::kAffWeightBias : (p.flags & RN_WEIGHT) ? rn::kAffWeight : rn::kAffNone;
+  const bool f32 = p.affine_dtype == RN_DTYPE_F32;
+  const int aff = (p.flags & RN_BIAS)     ? (f32 ? rn::kAffWB32 : rn::kAffWB16)
+                  : (p.flags & RN_WEIGHT) ? (f32 ? rn::kAffW32 : rn::kAffW16)
+                                          : rn::kAffNone;
   const bool rms = p.flags & RN_RMS;
-  if (p.fused) {
-    const bool gate = p.flags & RN_GATE;
-    return rms ? rn::fused_rms_kernel(gate, aff, vi) : rn::fused_ln_kernel(gate, aff, vi);
-  }
-  return rms ? rn::nss_rms_kernel(aff, vi) : rn::nss_ln_kernel(aff, vi);
+  const int out = p.y_dtype == RN_DTYPE_FP8_E4M3 ? rn::kOutFp8
+                  : p.y_dtype == RN_DTYPE_F32     ? rn::kOutF32
+                                                  : rn::kOutBf16;
+  if (p.fused) return rn::fused_kernel(rms, out, p.flags & RN_GATE, aff, vi);
+  return rn::nss_kernel(rms, out, aff, vi);
 }
 
 uint32_t tokens_per_frame(rn_layout lay, int64_t L) {
@@ -216,7 +235,7 @@ rn_status run(const Problem& p, void* stream) {
   if (st != RN_OK) return st;
   const int64_t R = p.B * p.L;
   if (R == 0) return RN_OK;
-  const int vi = shape_for(p.D, p.flags, p.fused,
+  const int vi = shape_for(p.D, p.flags, p.fused, p.affine_dtype,
                            hbm_streams(p.flags, p.fused, p.gate_layout, p.ss_layout));
   rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
   if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
@@ -231,6 +250,7 @@ rn_status run(const Problem& p, void* stream) {
   a.shift = p.shift;
   a.y = p.y;
   a.residual_out = p.residual_out;
+  a.y_scale = p.y_scale;
   a.rows = (uint32_t)R;
   a.L = (uint32_t)p.L;
   a.d = (uint32_t)p.D;
@@ -257,21 +277,75 @@ rn_status run(const Problem& p, void* stream) {
 
 extern "C" {
 
+static void apply_ext(Problem& p, const rn_ext* ext) {
+  p.affine_dtype = ext ? ext->affine_dtype : RN_DTYPE_BF16;
+  p.y_dtype = ext ? ext->y_dtype : RN_DTYPE_BF16;
+  p.y_scale = ext ? (float*)ext->y_scale : nullptr;
+}
+
+rn_status resnorm_fused_fwd_ex(void* y, void* residual_out, const void* x, const void* residual,
+                               const void* gate, const void* weight, const void* bias,
+                               const void* scale, const void* shift, int64_t B, int64_t L,
+                               int64_t D, uint32_t flags, rn_layout gate_layout,
+                               rn_layout ss_layout, float eps, const rn_ext* ext, void* stream) {
+  Problem p{};
+  p.fused = true;
+  p.y = y;
+  p.residual_out = residual_out;
+  p.x = x;
+  p.residual = residual;
+  p.gate = gate;
+  p.weight = weight;
+  p.bias = bias;
+  p.scale = scale;
+  p.shift = shift;
+  p.B = B;
+  p.L = L;
+  p.D = D;
+  p.flags = flags;
+  p.gate_layout = gate_layout;
+  p.ss_layout = ss_layout;
+  p.eps = eps;
+  apply_ext(p, ext);
+  return run(p, stream);
+}
+
+rn_status norm_scale_shift_fwd_ex(void* y, const void* x, const void* weight, const void* bias,
+                                  const void* scale, const void* shift, int64_t B, int64_t L,
+                                  int64_t D, uint32_t flags, rn_layout ss_layout, float eps,
+                                  const rn_ext* ext, void* stream) {
+  Problem p{};
+  p.fused = false;
+  p.y = y;
+  p.x = x;
+  p.weight = weight;
+  p.bias = bias;
+  p.scale = scale;
+  p.shift = shift;
+  p.B = B;
+  p.L = L;
+  p.D = D;
+  p.flags = flags;
+  p.gate_layout = rn_layout{RN_BCAST, 0};
+  p.ss_layout = ss_layout;
+  p.eps = eps;
+  apply_ext(p, ext);
+  return run(p, stream);
+}
+
 rn_status resnorm_fused_fwd(void* y, void* residual_out, const void* x, const void* residual,
                             const void* gate, const void* weight, const void* bias, const void* scale,
                             const void* shift, int64_t B, int64_t L, int64_t D, uint32_t flags,
                             rn_layout gate_layout, rn_layout ss_layout, float eps, void* stream) {
-  Problem p{true, y, residual_out, x, residual, gate, weight, bias, scale, shift,
-            B, L, D, flags, gate_layout, ss_layout, eps};
-  return run(p, stream);
+  return resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                              flags, gate_layout, ss_layout, eps, nullptr, stream);
 }
 
 rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const void* bias,
                                const void* scale, const void* shift, int64_t B, int64_t L, int64_t D,
                                uint32_t flags, rn_layout ss_layout, float eps, void* stream) {
-  Problem p{false, y, nullptr, x, nullptr, nullptr, weight, bias, scale, shift,
-            B, L, D, flags, rn_layout{RN_BCAST, 0}, ss_layout, eps};
-  return run(p, stream);
+  return norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags, ss_layout, eps,
+                                 nullptr, stream);
 }
 
 const char* rn_last_error(void) { return g_err; }
@@ -282,7 +356,8 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   if (!info) return fail(RN_EINVAL, "info is NULL");
   rn_status st = check_shape(B, L, D, flags, fused != 0);
   if (st != RN_OK) return st;
-  const int vi = shape_for(D, flags, fused != 0, hbm_streams(flags, fused != 0, gate_layout, ss_layout));
+  const int vi = shape_for(D, flags, fused != 0, RN_DTYPE_BF16,
+                           hbm_streams(flags, fused != 0, gate_layout, ss_layout));
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
   const rn::Shape s = rn::kShapes[vi];
   info->vec_per_lane = s.vpt;
@@ -294,6 +369,6 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   return RN_OK;
 }
 
-const char* rn_version(void) { return "resnorm 0.1.0 gfx950"; }
+const char* rn_version(void) { return "resnorm 0.2.0 gfx950"; }
 
 }  // extern "C"

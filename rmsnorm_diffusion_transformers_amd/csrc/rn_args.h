@@ -53,6 +53,7 @@ struct RowArgs {
   const void* shift;
   void* y;
   void* residual_out;
+  float* y_scale;      // FP8 output: per-row scale (else unused)
   uint32_t rows;       // B * L
   uint32_t L;          // tokens per batch
   uint32_t d;          // row width in elements (multiple of 8)
@@ -69,14 +70,17 @@ struct RowArgs {
 
 typedef void (*KernelFn)(RowArgs);
 
-// Affine variants.
-enum { kAffNone = 0, kAffWeight = 1, kAffWeightBias = 2 };
+// Affine variants: none, bf16 weight, bf16 weight + bias, binary32 weight,
+// binary32 weight + bias.
+enum { kAffNone = 0, kAffW16 = 1, kAffWB16 = 2, kAffW32 = 3, kAffWB32 = 4 };
+constexpr int kNumAff = 5;
 
-// Kernel lookup; each returns nullptr for an uncompiled combination.
-// shape indexes kShapes.
-KernelFn fused_ln_kernel(bool gate, int aff, int shape);
-KernelFn fused_rms_kernel(bool gate, int aff, int shape);
-KernelFn nss_ln_kernel(int aff, int shape);
-KernelFn nss_rms_kernel(int aff, int shape);
+// Output types of y.
+enum { kOutBf16 = 0, kOutF32 = 1, kOutFp8 = 2 };
+
+// Kernel lookup; nullptr for an uncompiled combination.  shape indexes
+// kShapes; out is a kOut* value.
+KernelFn fused_kernel(bool rms, int out, bool gate, int aff, int shape);
+KernelFn nss_kernel(bool rms, int out, int aff, int shape);
 
 }  // namespace rn

@@ -1,0 +1,10 @@
+// Compiled kernels: fused residual LayerNorm with gate, binary32 output, every affine variant and shape.
+#include "rn_row_kernel.hpp"
+
+namespace rn {
+
+KernelFn kernels_fused_ln_gate_f32(int aff, int shape) {
+  return kernel_for<false, true, true, kOutF32>(aff, shape);
+}
+
+}  // namespace rn

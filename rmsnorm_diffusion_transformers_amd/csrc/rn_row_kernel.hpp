@@ -40,6 +40,10 @@
 //     row ends with the bit-identical total.
 //   * fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even; fp32
 //     denormals are kept in these kernels).
+//   * Output y is bf16, binary32, or OCP FP8 E4M3 with a per-row scale
+//     max|t| / 448 (compile-time; the FP8 kernels take a row maximum before
+//     converting with v_cvt_pk_fp8_f32).
+//   * weight / bias are bf16 or binary32 (compile-time).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -102,36 +106,46 @@ __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the 64 lanes of a wave; every lane returns the same bits.  Each
-// step adds a lane's value to its partner's in an order that is the same on
-// both partners, so the result is identical across lanes.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]: partner lane ^ 1
-  v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]: partner lane ^ 2
-  v += dpp<0x141>(v);  // row_half_mirror: the other quad of the 8-lane group
-  v += dpp<0x140>(v);  // row_mirror: the other 8-lane half of the 16-lane row
+struct Add {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct Max {
+  __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
+};
+
+// Reduction over the 64 lanes of a wave; every lane returns the same bits.
+// Each step combines a lane's value with its partner's in an order that is
+// the same on both partners, so the result is identical across lanes.
+template <class OPR>
+__device__ __forceinline__ float wave_reduce(float v, OPR op) {
+  v = op(v, dpp<0xB1>(v));   // quad_perm [1,0,3,2]: partner lane ^ 1
+  v = op(v, dpp<0x4E>(v));   // quad_perm [2,3,0,1]: partner lane ^ 2
+  v = op(v, dpp<0x141>(v));  // row_half_mirror: the other quad of the 8-lane group
+  v = op(v, dpp<0x140>(v));  // row_mirror: the other 8-lane half of the 16-lane row
   {
     auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // rows 2k and 2k+1
+    v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));  // rows 2k and 2k+1
   }
   {
     auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = __uint_as_float(p[0]) + __uint_as_float(p[1]);  // lanes 0-31 and 32-63
+    v = op(__uint_as_float(p[0]), __uint_as_float(p[1]));  // lanes 0-31 and 32-63
   }
   return v;
 }
 
-// Total over the W waves of one row.  Each wave's total goes to LDS; after the
-// barrier every wave of the row adds the W partials in the same order.
-template <int W>
-__device__ __forceinline__ float row_sum(float v, float* red, uint32_t wave, uint32_t slot) {
-  v = wave_sum(v);
+// Reduction over the W waves of one row.  Each wave's result goes to LDS;
+// after the barrier every wave of the row combines the W partials in the same
+// order.
+template <int W, class OPR>
+__device__ __forceinline__ float row_reduce(float v, OPR op, float* red, uint32_t wave,
+                                            uint32_t slot) {
+  v = wave_reduce(v, op);
   if constexpr (W > 1) {
     if ((threadIdx.x & (kWaveSize - 1)) == 0) red[wave] = v;
     __syncthreads();
     v = red[slot * W];
 #pragma unroll
-    for (int p = 1; p < W; ++p) v += red[slot * W + p];
+    for (int p = 1; p < W; ++p) v = op(v, red[slot * W + p]);
   }
   return v;
 }
@@ -144,18 +158,65 @@ __device__ __forceinline__ uint32_t mod_row(int32_t kind, uint32_t frames, uint3
   return b * frames + l / tpf;
 }
 
-template <bool RMS, bool FUSED, bool GATE, int AFF, int VPT, int W, int RPB, int PL, int PS>
-__global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs a) {
+// What a kernel computes: LayerNorm or RMSNorm, fused residual or norm-only,
+// gate, affine variant, output type.
+template <bool RMS_, bool FUSED_, bool GATE_, int AFF_, int OUT_>
+struct Op {
+  static constexpr bool rms = RMS_;
+  static constexpr bool fused = FUSED_;
+  static constexpr bool gate = GATE_;
+  static constexpr bool has_w = AFF_ != kAffNone;
+  static constexpr bool has_b = AFF_ == kAffWB16 || AFF_ == kAffWB32;
+  static constexpr bool aff32 = AFF_ == kAffW32 || AFF_ == kAffWB32;
+  static constexpr int out = OUT_;
+};
+
+// An affine operand (weight or bias) for VPT vectors of 8 elements: bf16
+// (one 16-byte vector each) or binary32 (two).
+template <bool F32, int VPT>
+struct AffineRow {
+  u32x4 v[VPT][F32 ? 2 : 1];
+  template <int PL>
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, uint32_t base) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if constexpr (F32) {
+        v[i][0] = load16<kPolicyDefault, PL>(r, base * 2u + i * 2048u);
+        v[i][1] = load16<kPolicyDefault, PL>(r, base * 2u + i * 2048u + 16u);
+      } else {
+        v[i][0] = load16<kPolicyDefault, PL>(r, base + i * 1024u);
+      }
+    }
+  }
+  // element 2j (lo) and 2j+1 (hi) of vector i
+  __device__ __forceinline__ float lo(int i, int j) const {
+    if constexpr (F32) return __uint_as_float(v[i][j >> 1][(j & 1) * 2]);
+    else return lo_f32(v[i][0][j]);
+  }
+  __device__ __forceinline__ float hi(int i, int j) const {
+    if constexpr (F32) return __uint_as_float(v[i][j >> 1][(j & 1) * 2 + 1]);
+    else return hi_f32(v[i][0][j]);
+  }
+};
+
+template <class OP, int SHAPE>
+__global__ __launch_bounds__(kWaveSize * kShapes[SHAPE].w * kShapes[SHAPE].rpb)
+void row_kernel(const RowArgs a) {
+  constexpr int W = kShapes[SHAPE].w;
+  constexpr int VPT = kShapes[SHAPE].vpt;
+  constexpr int RPB = kShapes[SHAPE].rpb;
+  constexpr int PL = kPaceLoads;
+  constexpr int PS = kPaceStores;
   static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
-  constexpr int kRowsPerBlock = RPB;
   [[maybe_unused]] __shared__ float red_sum[W * RPB];
   [[maybe_unused]] __shared__ float red_sq[W * RPB];
+  [[maybe_unused]] __shared__ float red_max[W * RPB];
 
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & (kWaveSize - 1);
   const uint32_t slot = wave / W;  // row slot in the workgroup
   const uint32_t part = wave % W;  // which contiguous part of the row this wave holds
-  const uint32_t row = blockIdx.x * kRowsPerBlock + slot;
+  const uint32_t row = blockIdx.x * RPB + slot;
   // With W > 1 every wave must reach the barriers, so a wave past the last
   // row keeps going with its memory operations disabled (zero-range buffers).
   const bool live = row < a.rows;
@@ -168,11 +229,10 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
   const uint32_t b = r / a.L;
   const uint32_t l = r - b * a.L;
   const uint32_t srow = mod_row(a.ss_kind, a.ss_frames, a.ss_tokens_per_frame, r, b, l);
-  // lane-local byte offset of vector v: this wave's part, then 1 KB per vector
+  // lane-local byte offset of vector v (bf16): this wave's part, then 1 KB per vector
   const uint32_t base = (part * VPT * kWaveSize + lane) * 16u;
 
   const auto rs_x = row_rsrc((const char*)a.x + row_off, row_bytes);
-  const auto rs_y = row_rsrc((const char*)a.y + row_off, row_bytes);
   const auto rs_sc = row_rsrc((const char*)a.scale + (uint64_t)srow * (a.d * 2u), row_bytes);
   const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * (a.d * 2u), row_bytes);
 
@@ -180,16 +240,15 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
   u32x4 h[VPT];  // x (norm-only) or residual, later the bf16-packed residual_out
   [[maybe_unused]] u32x4 xv[VPT];
   [[maybe_unused]] u32x4 gv[VPT];
-  [[maybe_unused]] u32x4 wv[VPT];
-  [[maybe_unused]] u32x4 bv[VPT];
+  [[maybe_unused]] AffineRow<OP::aff32, VPT> wv, bv;
   u32x4 sc[VPT], sh[VPT];
-  if constexpr (FUSED) {
+  if constexpr (OP::fused) {
     const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_r, base + v * 1024u);
-    if constexpr (GATE) {
+    if constexpr (OP::gate) {
       const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, r, b, l);
       const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * (a.d * 2u), row_bytes);
 #pragma unroll
@@ -199,16 +258,9 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
 #pragma unroll
     for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
   }
-  if constexpr (AFF >= kAffWeight) {
-    const auto rs_w = row_rsrc(a.weight, row_bytes);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) wv[v] = load16<kPolicyDefault, PL>(rs_w, base + v * 1024u);
-  }
-  if constexpr (AFF >= kAffWeightBias) {
-    const auto rs_b = row_rsrc(a.bias, row_bytes);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) bv[v] = load16<kPolicyDefault, PL>(rs_b, base + v * 1024u);
-  }
+  const uint32_t aff_bytes = live ? a.d * (OP::aff32 ? 4u : 2u) : 0u;
+  if constexpr (OP::has_w) wv.template load<PL>(row_rsrc(a.weight, aff_bytes), base);
+  if constexpr (OP::has_b) bv.template load<PL>(row_rsrc(a.bias, aff_bytes), base);
   // per-row scale/shift stream like the activations; shared rows stay cached
   if (a.ss_kind == 1) {
 #pragma unroll
@@ -223,7 +275,7 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
   }
 
   // ---- residual update (fused) ----
-  if constexpr (FUSED) {
+  if constexpr (OP::fused) {
     const auto rs_ro = row_rsrc((const char*)a.residual_out + row_off, row_bytes);
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
@@ -231,7 +283,7 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         float s0, s1;
-        if constexpr (GATE) {
+        if constexpr (OP::gate) {
           // gate * x is exact in binary32 (8-bit x 8-bit significands), so the
           // fused multiply-add rounds exactly once, like residual + (gate * x).
           s0 = __builtin_fmaf(lo_f32(gv[v][j]), lo_f32(xv[v][j]), lo_f32(h[v][j]));
@@ -251,13 +303,13 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
   const float inv_d = 1.0f / (float)a.d;
   float mean = 0.f;
   float sq = 0.f;
-  if constexpr (!RMS) {
+  if constexpr (!OP::rms) {
     float sum = 0.f;
 #pragma unroll
     for (int v = 0; v < VPT; ++v)
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
-    mean = row_sum<W>(sum, red_sum, wave, slot) / (float)a.d;
+    mean = row_reduce<W>(sum, Add{}, red_sum, wave, slot) / (float)a.d;
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       float part_sq = 0.f;
@@ -283,41 +335,93 @@ __global__ __launch_bounds__(kWaveSize * W * RPB) void row_kernel(const RowArgs 
         sq = __builtin_fmaf(h1, h1, sq);
       }
   }
-  float var = row_sum<W>(sq, red_sq, wave, slot) * inv_d;
+  float var = row_reduce<W>(sq, Add{}, red_sq, wave, slot) * inv_d;
   var = var > 0.f ? var : 0.f;
   const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
 
-  // ---- epilogue from the register cache ----
-#pragma unroll
-  for (int v = 0; v < VPT; ++v) {
-    u32x4 o;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float n0 = (lo_f32(h[v][j]) - mean) * rstd;
-      float n1 = (hi_f32(h[v][j]) - mean) * rstd;
-      if constexpr (AFF == kAffWeight) {
-        n0 *= lo_f32(wv[v][j]);
-        n1 *= hi_f32(wv[v][j]);
-      } else if constexpr (AFF == kAffWeightBias) {
-        n0 = __builtin_fmaf(n0, lo_f32(wv[v][j]), lo_f32(bv[v][j]));
-        n1 = __builtin_fmaf(n1, hi_f32(wv[v][j]), hi_f32(bv[v][j]));
-      }
-      const float t0 = __builtin_fmaf(n0, 1.0f + lo_f32(sc[v][j]), lo_f32(sh[v][j]));
-      const float t1 = __builtin_fmaf(n1, 1.0f + hi_f32(sc[v][j]), hi_f32(sh[v][j]));
-      o[j] = pack_bf16(t0, t1);
+  // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v
+  auto tval = [&](int v, int j, int k) -> float {
+    const float hv = k ? hi_f32(h[v][j]) : lo_f32(h[v][j]);
+    float n = (hv - mean) * rstd;
+    if constexpr (OP::has_w && OP::has_b) {
+      n = __builtin_fmaf(n, k ? wv.hi(v, j) : wv.lo(v, j), k ? bv.hi(v, j) : bv.lo(v, j));
+    } else if constexpr (OP::has_w) {
+      n *= k ? wv.hi(v, j) : wv.lo(v, j);
     }
-    store16<kPolicyStream, PS>(o, rs_y, base + v * 1024u);
+    const float s = k ? hi_f32(sc[v][j]) : lo_f32(sc[v][j]);
+    const float t = k ? hi_f32(sh[v][j]) : lo_f32(sh[v][j]);
+    return __builtin_fmaf(n, 1.0f + s, t);
+  };
+
+  // ---- epilogue from the register cache ----
+  if constexpr (OP::out == kOutBf16) {
+    {
+      const auto rs_y = row_rsrc((const char*)a.y + row_off, row_bytes);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = pack_bf16(tval(v, j, 0), tval(v, j, 1));
+        store16<kPolicyStream, PS>(o, rs_y, base + v * 1024u);
+      }
+    }
+  } else if constexpr (OP::out == kOutF32) {
+    {
+      // binary32 y: 32 bytes per lane per vector, two 16-byte stores
+      const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)r * (a.d * 4u), live ? a.d * 4u : 0u);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        u32x4 o0, o1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          o0[2 * j] = __float_as_uint(tval(v, j, 0));
+          o0[2 * j + 1] = __float_as_uint(tval(v, j, 1));
+          o1[2 * j] = __float_as_uint(tval(v, j + 2, 0));
+          o1[2 * j + 1] = __float_as_uint(tval(v, j + 2, 1));
+        }
+        store16<kPolicyStream, PS>(o0, rs_y, base * 2u + v * 2048u);
+        store16<kPolicyStream, PS>(o1, rs_y, base * 2u + v * 2048u + 16u);
+      }
+    }
+  } else {
+    // FP8 E4M3 y with a per-row scale: the row maximum of |t| first (lanes
+    // past a ragged row's end are left out), then t * 448 / max converted.
+    float amax = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(tval(v, j, 0)),
+                                               __builtin_fabsf(tval(v, j, 1))));
+      amax = (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? __builtin_fmaxf(amax, m) : amax;
+    }
+    amax = row_reduce<W>(amax, Max{}, red_max, wave, slot);
+    const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+    const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)r * a.d, live ? a.d : 0u);
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      uint32_t w0 = 0, w1 = 0;
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 0, 0) * inv, tval(v, 0, 1) * inv, w0, false);
+      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 1, 0) * inv, tval(v, 1, 1) * inv, w0, true);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 2, 0) * inv, tval(v, 2, 1) * inv, w1, false);
+      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 3, 0) * inv, tval(v, 3, 1) * inv, w1, true);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64((u32x2){w0, w1}, rs_y, base / 2u + v * 512u, 0,
+                                            kPolicyStream);
+      pace<PS>();
+    }
+    if (live && part == 0 && lane == 0) a.y_scale[r] = amax / 448.0f;
   }
 }
 
-// Table of one flag combination over every compiled shape.
-template <bool RMS, bool FUSED, bool GATE, int AFF>
+// Table of one operation over every compiled shape.
+template <class OP>
 KernelFn kernel_for_shape(int shape) {
   switch (shape) {
 #define RN_CASE(i) \
   case i:          \
-    return row_kernel<RMS, FUSED, GATE, AFF, kShapes[i].vpt, kShapes[i].w, kShapes[i].rpb, \
-                      kPaceLoads, kPaceStores>;
+    return row_kernel<OP, i>;
     RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
     RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
     RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18)
@@ -328,5 +432,18 @@ KernelFn kernel_for_shape(int shape) {
 }
 
 static_assert(kNumShapes == 19, "kernel_for_shape lists every shape");
+
+// Table of one (norm, op, gate, output) family over the affine variants.
+template <bool RMS, bool FUSED, bool GATE, int OUT>
+KernelFn kernel_for(int aff, int shape) {
+  switch (aff) {
+    case kAffNone: return kernel_for_shape<Op<RMS, FUSED, GATE, kAffNone, OUT>>(shape);
+    case kAffW16: return kernel_for_shape<Op<RMS, FUSED, GATE, kAffW16, OUT>>(shape);
+    case kAffWB16: return kernel_for_shape<Op<RMS, FUSED, GATE, kAffWB16, OUT>>(shape);
+    case kAffW32: return kernel_for_shape<Op<RMS, FUSED, GATE, kAffW32, OUT>>(shape);
+    case kAffWB32: return kernel_for_shape<Op<RMS, FUSED, GATE, kAffWB32, OUT>>(shape);
+    default: return nullptr;
+  }
+}
 
 }  // namespace rn

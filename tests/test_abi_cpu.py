@@ -215,3 +215,45 @@ def test_inputs_may_share_memory(rn):
     assert st == 0, err
     st, err = fused(rn, B=0, shift=addr(7), gate=addr(7))
     assert st == 0, err
+
+
+def fused_ex(rn, affine_dtype=0, y_dtype=0, y_scale=None, **kw):
+    args = dict(y=addr(0), residual_out=addr(1), x=addr(2), residual=addr(3), gate=addr(4),
+                weight=None, bias=None, scale=addr(7), shift=addr(8), B=1, L=16, D=5120,
+                flags=rn.RN_GATE, gate_layout=(rn.RN_BCAST, 0), ss_layout=(rn.RN_BCAST, 0),
+                eps=1e-6)
+    args.update(kw)
+    ext = rn.rn_ext(affine_dtype, y_dtype, y_scale)
+    st = rn._lib.resnorm_fused_fwd_ex(args["y"], args["residual_out"], args["x"],
+                                      args["residual"], args["gate"], args["weight"],
+                                      args["bias"], args["scale"], args["shift"], args["B"],
+                                      args["L"], args["D"], args["flags"],
+                                      rn._layout(args["gate_layout"]),
+                                      rn._layout(args["ss_layout"]), args["eps"],
+                                      ctypes.byref(ext), None)
+    return st, rn.last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(affine_dtype=2), 1, "affine_dtype"),
+    (dict(affine_dtype=-1), 1, "affine_dtype"),
+    (dict(y_dtype=3), 1, "y_dtype"),
+    (dict(y_dtype=2), 1, "needs y_scale"),
+    (dict(y_dtype=1, y_scale=addr(9)), 1, "y_scale given"),
+    (dict(y_dtype=2, y_scale=addr(9) + 2), 1, "y_scale is not 4-byte aligned"),
+    (dict(y_dtype=2, y_scale=addr(2)), 1, "y_scale overlaps x"),
+    (dict(y_dtype=1, y=addr(2)), 1, "y overlaps x"),      # binary32 y cannot alias bf16 x
+    (dict(y_dtype=1, y=addr(1) - 5120 * 2 * 16), 1, "overlaps"),  # 2x wider y runs into residual_out
+])
+def test_fused_ex_rejects(rn, kw, status, msg):
+    st, err = fused_ex(rn, **kw)
+    assert st == status, (st, err)
+    assert msg in err, err
+
+
+def test_ex_empty_problem_and_null_ext(rn):
+    assert fused_ex(rn, B=0, y_dtype=2, y_scale=addr(9))[0] == 0
+    assert fused_ex(rn, B=0, affine_dtype=1, flags=rn.RN_GATE | rn.RN_WEIGHT, weight=addr(5))[0] == 0
+    st = rn._lib.norm_scale_shift_fwd_ex(addr(0), addr(2), None, None, addr(7), addr(8), 0, 4,
+                                         64, 0, rn._layout((0, 0)), 1e-6, None, None)
+    assert st == 0, rn.last_error()
