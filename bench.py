@@ -11,9 +11,17 @@ Metric: algorithmic HBM bytes (every operand read once + every output written
 once) / time, in GB/s (1e9 B/s), against the 8 TB/s HBM3E peak.  The
 norm-only companion (same shape, broadcast scale/shift) is reported beside it.
 
+Beside the headline the line carries: the norm-only companion; variants of
+the op at the same shape (broadcast modulation with and without binary32
+weight+bias, FP8 and binary32 outputs, per-batch modulation); a DiT-forward
+mix of the three calls WAN2.2 makes per forward (41 norm-only + 40 fused with
+affine + 40 fused without, broadcast modulation, as in sglang PR #36349,
+"Microbenchmark") against the pages' per-forward total; a plain-copy
+reference; and the CPU oracle baseline.
+
 Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
 GPU), --steps K, --warmup W, --calibrate (time a plain elementwise copy, used to
-scale rocprof byte counters), --no-cpu-baseline, --workload NAME.
+scale rocprof byte counters), --no-cpu-baseline, --no-extras, --workload NAME.
 """
 from __future__ import annotations
 
@@ -74,7 +82,26 @@ def upload(inp, dev):
             for k, v in inp.items()}
 
 
-def time_workload(rn, wl, steps, warmup, dev):
+def time_calls(fn, steps, warmup):
+    """Average ms per call of fn() over `steps` calls after `warmup`, timed
+    with events on the current stream (the stream the kernels run on)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - w0
+
+
+def time_workload(rn, wl, steps, warmup, dev, keep=False):
     import torch
 
     import synth
@@ -87,22 +114,104 @@ def time_workload(rn, wl, steps, warmup, dev):
     y = torch.empty_like(d["x"])
     ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        launch_workload(rn, wl, d, y, ro, stream)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
-        launch_workload(rn, wl, d, y, ro, stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = start.elapsed_time(end) / steps
+    ms, wall = time_calls(lambda: launch_workload(rn, wl, d, y, ro, stream), steps, warmup)
+    if keep:
+        return ms, wall, (d, y, ro)
     del d, y, ro
     torch.cuda.empty_cache()
     return ms, wall
+
+
+def extras(rn, dev_tensors, steps, warmup):
+    """Variants of the op and the DiT-forward mix at the headline shape, on the
+    headline's resident x / residual (B 1, L 176400, D 5120)."""
+    import numpy as np
+    import torch
+
+    import synth
+    d, y, ro = dev_tensors
+    x, res = d["x"], d["residual"]
+    R, D = x.shape
+    dev = x.device
+    wl = synth.WORKLOADS[HEADLINE]
+    bc = {k: synth.fill(wl.dists[t], 99, D).reshape(1, D) for k, t in
+          (("gate", synth.GATE), ("scale", synth.SCALE), ("shift", synth.SHIFT))}
+    bc = upload(bc, dev)
+    rng = np.random.default_rng(99)
+    w32 = torch.from_numpy((1.0 + 0.05 * rng.standard_normal(D)).astype(np.float32)).to(dev)
+    b32 = torch.from_numpy((0.1 * rng.standard_normal(D)).astype(np.float32)).to(dev)
+    G, W, Bi = rn.RN_GATE, rn.RN_WEIGHT, rn.RN_BIAS
+    F32, FP8 = rn.RN_DTYPE_F32, rn.RN_DTYPE_FP8_E4M3
+    BC, FR = (rn.RN_BCAST, 0), (rn.RN_FRAME, 49)
+    y32 = torch.empty((R, D), dtype=torch.float32, device=dev)
+    y8 = torch.empty((R, D), dtype=torch.float8_e4m3fn, device=dev)
+    ys = torch.empty((R,), dtype=torch.float32, device=dev)
+
+    def fused_bcast():
+        rn.resnorm_fused_fwd(y, ro, x, res, bc["gate"], None, None, bc["scale"], bc["shift"],
+                             1, R, D, G, BC, BC, 1e-6)
+
+    def fused_affine():
+        rn.resnorm_fused_fwd_ex(y, ro, x, res, bc["gate"], w32, b32, bc["scale"], bc["shift"],
+                                1, R, D, G | W | Bi, BC, BC, 1e-6, F32)
+
+    def nss_bcast():
+        rn.norm_scale_shift_fwd(y, x, None, None, bc["scale"], bc["shift"], 1, R, D, 0, BC, 1e-6)
+
+    def frame_fp8():
+        rn.resnorm_fused_fwd_ex(y8, ro, x, res, d["gate"], None, None, d["scale"], d["shift"],
+                                1, R, D, G, FR, FR, 1e-6, y_dtype=FP8, y_scale=ys)
+
+    def frame_f32():
+        rn.resnorm_fused_fwd_ex(y32, ro, x, res, d["gate"], None, None, d["scale"], d["shift"],
+                                1, R, D, G, FR, FR, 1e-6, y_dtype=F32)
+
+    pb = {k: v.expand(4, D).contiguous() for k, v in bc.items()}   # (4, D): per batch
+
+    def per_batch():
+        rn.resnorm_fused_fwd(y, ro, x, res, pb["gate"], None, None, pb["scale"], pb["shift"],
+                             4, R // 4, D, G, (rn.RN_FRAME, 1), (rn.RN_FRAME, 1), 1e-6)
+
+    act = R * D * 2
+    row = D * 2
+    cases = [
+        ("fused_ln_bcast", "fused LN, gate/scale/shift (1,C)", fused_bcast, 4 * act + 3 * row),
+        ("fused_ln_bcast_affine_fp32", "fused LN + fp32 weight/bias, (1,C) modulation",
+         fused_affine, 4 * act + 3 * row + 2 * 4 * D),
+        ("fused_ln_frame_fp8_out", "headline op, FP8 E4M3 y + per-row scale", frame_fp8,
+         3 * act + R * D + 4 * R + 3 * 49 * row),
+        ("fused_ln_frame_fp32_out", "headline op, binary32 y", frame_f32,
+         3 * act + 2 * act + 3 * 49 * row),
+        ("fused_ln_per_batch_b4", "fused LN, B 4 x L 44100, (B,1,C) modulation", per_batch,
+         4 * act + 3 * 4 * row),
+    ]
+    out = []
+    for name, what, fn, nbytes in cases:
+        ms, _ = time_calls(fn, max(10, steps // 4), max(3, warmup // 4))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log("%s: %.4f ms/launch, %.1f GB/s" % (name, ms, gbs))
+        out.append({"variant": name, "what": what, "ms_per_launch": round(ms, 5),
+                    "algorithmic_bytes": nbytes, "GB/s": round(gbs, 1),
+                    "frac": round(gbs / HBM_PEAK_GBS, 4)})
+
+    # DiT forward: per block norm1 (norm-only), self-attention norm (fused,
+    # affine), cross-attention norm (fused, no affine); norm_out at the end.
+    def forward():
+        for _ in range(40):
+            nss_bcast()
+            fused_affine()
+            fused_bcast()
+        nss_bcast()
+
+    fwd_ms, _ = time_calls(forward, 3, 1)
+    log("DiT forward mix: %.2f ms per forward (121 calls)" % fwd_ms)
+    mix = {"ms_per_forward": round(fwd_ms, 3),
+           "calls": {"norm_scale_shift (no affine)": 41, "fused, fp32 affine": 40,
+                     "fused, no affine": 40},
+           "shape": "B 1, L 176400, D 5120, broadcast (1,C) gate/scale/shift, LayerNorm",
+           "pages_prior_art_ms_per_forward_context": [171.6, 174.8]}
+    del y32, y8, ys, bc, pb, w32, b32
+    return out, mix
 
 
 def flags_of(rn, wl):
@@ -208,6 +317,7 @@ def main():
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-companion", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures this path on exactly one GPU (the row-wise op needs no "
@@ -224,7 +334,14 @@ def main():
     import rmsnorm_diffusion_transformers_amd as rn
     import synth
     wl = synth.WORKLOADS[args.workload]
-    ms, wall = time_workload(rn, wl, args.steps, args.warmup, dev)
+    want_extras = not args.no_extras and args.workload == HEADLINE
+    if want_extras:
+        ms, wall, kept = time_workload(rn, wl, args.steps, args.warmup, dev, keep=True)
+        variants, mix = extras(rn, kept, args.steps, args.warmup)
+        del kept
+        torch.cuda.empty_cache()
+    else:
+        ms, wall = time_workload(rn, wl, args.steps, args.warmup, dev)
     nbytes = wl.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("%s: %.4f ms/launch, %.1f GB/s (%.1f%% of %g)" % (wl.name, ms, gbs, 100 * gbs / HBM_PEAK_GBS,
@@ -266,6 +383,9 @@ def main():
         "companions": companions,
         "copy_reference": ref,
     }
+    if want_extras:
+        line["variants"] = variants
+        line["dit_forward_mix"] = mix
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

@@ -29,9 +29,9 @@ struct Shape {
   int rpb;
 };
 constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1, 5, 4},
-                             {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 6, 2},  {2, 8, 2},
-                             {2, 10, 2}, {4, 4, 1},  {4, 5, 1},  {4, 6, 1},  {4, 8, 1},
-                             {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
+                             {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 5, 2},  {2, 6, 2},
+                             {2, 8, 2},  {2, 10, 2}, {4, 4, 1},  {4, 5, 1},  {4, 6, 1},
+                             {4, 8, 1},  {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
 constexpr int kManyStreamsMinD = 2560;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at

@@ -379,8 +379,10 @@ void row_kernel(const RowArgs a) {
           o1[2 * j] = __float_as_uint(tval(v, j + 2, 0));
           o1[2 * j + 1] = __float_as_uint(tval(v, j + 2, 1));
         }
-        store16<kPolicyStream, PS>(o0, rs_y, base * 2u + v * 2048u);
-        store16<kPolicyStream, PS>(o1, rs_y, base * 2u + v * 2048u + 16u);
+        // each store covers every other 16-byte chunk of a 2 KB span; the
+        // default policy lets L2 merge the pair into whole lines
+        store16<kPolicyDefault, PS>(o0, rs_y, base * 2u + v * 2048u);
+        store16<kPolicyDefault, PS>(o1, rs_y, base * 2u + v * 2048u + 16u);
       }
     }
   } else {
@@ -424,14 +426,14 @@ KernelFn kernel_for_shape(int shape) {
     return row_kernel<OP, i>;
     RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
     RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
-    RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18)
+    RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18) RN_CASE(19)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumShapes == 19, "kernel_for_shape lists every shape");
+static_assert(kNumShapes == 20, "kernel_for_shape lists every shape");
 
 // Table of one (norm, op, gate, output) family over the affine variants.
 template <bool RMS, bool FUSED, bool GATE, int OUT>

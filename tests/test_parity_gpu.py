@@ -365,7 +365,7 @@ def test_every_compiled_shape(rn, orc):
     pick, at the first row width that selects it (a ragged row for most), with
     B=2, L=5 (so the last workgroup of a multi-row shape is partly empty)."""
     cases = _shape_cases(rn)
-    assert len(cases) == 19, sorted(cases)
+    assert len(cases) == 20, sorted(cases)
     for (w, vpt), (D, fused, flags, sl) in sorted(cases.items()):
         log("shape W=%d VPT=%d via D=%d fused=%s flags=%d ss=%s" % (w, vpt, D, fused, flags, sl))
         aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
