@@ -234,6 +234,41 @@ def launch_workload(rn, wl, d, y, ro, stream):
                                 d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps, stream)
 
 
+def small_batch_latency(rn, dev, names=("fused_ln_b1_l16_d5120", "fused_rms_w_b2_l16_d10240")):
+    """The L = 16 workloads are launch- and latency-bound (their bytes fit in
+    cache): per-call time of back-to-back launches on the stream, and with 100
+    launches captured in one HIP graph and replayed (wall time / 100)."""
+    import torch
+
+    import synth
+    out = []
+    for name in names:
+        wl = synth.WORKLOADS[name]
+        d = upload(synth.make_inputs(wl, threads=1), dev)
+        y = torch.empty_like(d["x"])
+        ro = torch.empty_like(d["x"])
+        stream = torch.cuda.current_stream()
+        eager_ms, _ = time_calls(lambda: launch_workload(rn, wl, d, y, ro, stream), 200, 20)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            launch_workload(rn, wl, d, y, ro, torch.cuda.current_stream())
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(100):
+                launch_workload(rn, wl, d, y, ro, torch.cuda.current_stream())
+        graph_ms, _ = time_calls(g.replay, 20, 3)
+        out.append({"workload": name, "us_per_call_stream": round(eager_ms * 1e3, 2),
+                    "us_per_call_graph": round(graph_ms * 1e3 / 100, 2),
+                    "algorithmic_bytes": wl.algorithmic_bytes()})
+        log("%s: %.2f us/call on the stream, %.2f us/call in a graph" % (
+            name, eager_ms * 1e3, graph_ms * 1e3 / 100))
+        del g, d, y, ro
+    return out
+
+
 def copy_reference(steps, warmup, dev):
     """A plain elementwise copy (torch.neg on bf16: reads N bytes, writes N
     bytes) on a tensor of the headline's activation size: the rocprof counter
@@ -386,6 +421,7 @@ def main():
     if want_extras:
         line["variants"] = variants
         line["dit_forward_mix"] = mix
+        line["small_batch_latency"] = small_batch_latency(rn, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(line), flush=True)

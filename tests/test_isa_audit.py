@@ -1,0 +1,102 @@
+"""Audit of the gfx950 assembly of the hot kernels (built here, on the CPU).
+
+The pages audit the prior-art kernel's ISA for 128-bit-only global traffic,
+no scratch, and the count of cross-lane steps (sglang PR #33144, "Speed Tests
+and Profiling").  The same invariants for this library's kernels, from the
+assembly hipcc writes for them:
+  * every global access is a 128-bit buffer load/store (no global_/flat_ or
+    narrower accesses; the FP8 output's 8-byte stores are the one exception,
+    in the FP8 kernels only);
+  * no scratch (private segment 0, no VGPR spills) and no LDS for one wave
+    per row;
+  * the wave reductions are DPP adds plus permlane16/permlane32 swaps;
+  * the instruction counts per row match the design: 10 vectors per lane of
+    each of x, residual, gate, and scale/shift (twice: the per-row and the
+    shared-row paths), 20 stores, 80 bf16 packs.
+"""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "rmsnorm_diffusion_transformers_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def _asm(tu, tmp_path):
+    out = tmp_path / (tu + ".s")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-I", CSRC,
+                    "--cuda-device-only", "-S", "-Xclang", "-target-feature", "-Xclang",
+                    "-packed-fp32-ops", "-o", str(out), os.path.join(CSRC, tu)],
+                   check=True, capture_output=True)
+    return out.read_text()
+
+
+def _kernel(asm, symbol):
+    """(instructions, metadata) of one kernel: the code from its label to
+    s_endpgm, and its kernel descriptor plus its entry in the code-object
+    metadata."""
+    m = re.search(r"^%s:[^\n]*\n(.*?)s_endpgm" % re.escape(symbol), asm, re.S | re.M)
+    assert m, symbol
+    body = m.group(1)
+    desc = re.search(r"\.amdhsa_kernel %s\n(.*?)\.end_amdhsa_kernel" % re.escape(symbol), asm, re.S)
+    entries = asm.split("amdhsa.kernels:")[1].split("\n  - ")
+    entry = [e for e in entries if re.search(r"\.name:\s+%s\n" % re.escape(symbol), e)]
+    return body, (desc.group(1) if desc else "") + "\n" + (entry[0] if entry else "")
+
+
+def _count(body, mnemonic):
+    return len(re.findall(r"^\s+%s\b" % re.escape(mnemonic), body, re.M))
+
+
+def _meta_int(meta, key):
+    m = re.search(r"\.%s:?\s+(\d+)" % key, meta)
+    return int(m.group(1)) if m else None
+
+
+@pytest.fixture(scope="module")
+def fused_asm(tmp_path_factory):
+    return _asm("rn_inst_fused_ln_gate_bf16.hip", tmp_path_factory.mktemp("asm"))
+
+
+HEADLINE = "_ZN2rn10row_kernelINS_2OpILb0ELb1ELb1ELi0ELi0EEELi7EEEvNS_7RowArgsE"
+
+
+def test_headline_kernel_memory_traffic_is_128bit(fused_asm):
+    body, meta = _kernel(fused_asm, HEADLINE)
+    assert not re.search(r"^\s+(global|flat|scratch)_", body, re.M)
+    assert not re.search(r"^\s+buffer_(load|store)_(dword|dwordx2|dwordx3|short|byte|ubyte|ushort|sbyte|sshort)\b", body, re.M)
+    assert _count(body, "buffer_load_dwordx4") == 70     # x, r, gate 10 each; scale/shift 20 on each path
+    assert _count(body, "buffer_store_dwordx4") == 20    # residual_out, y
+    assert _count(body, "v_cvt_pk_bf16_f32") == 80
+
+
+def test_headline_kernel_reductions_and_resources(fused_asm):
+    body, meta = _kernel(fused_asm, HEADLINE)
+    assert _count(body, "v_add_f32_dpp") == 8            # two reductions x four DPP steps
+    assert _count(body, "v_permlane16_swap_b32_e32") == 2
+    assert _count(body, "v_permlane32_swap_b32_e32") == 2
+    assert _count(body, "s_barrier") == 0                # one wave per row: no barrier
+    assert not re.search(r"^\s+ds_", body, re.M)         # no LDS
+    assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
+    assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == 0
+    assert _meta_int(meta, "vgpr_spill_count") == 0
+    assert _meta_int(meta, "sgpr_spill_count") == 0
+    assert _meta_int(meta, "vgpr_count") <= 256          # two waves per SIMD
+    assert _meta_int(meta, "amdhsa_float_denorm_mode_32") == 3   # fp32 denormals kept
+
+
+def test_fp8_kernel_stores(tmp_path):
+    asm = _asm("rn_inst_nss_ln_fp8.hip", tmp_path)
+    sym = "_ZN2rn10row_kernelINS_2OpILb0ELb0ELb0ELi0ELi2EEELi7EEEvNS_7RowArgsE"
+    body, meta = _kernel(asm, sym)
+    assert _count(body, "buffer_store_dwordx2") == 10    # 8 FP8 bytes per lane per vector
+    assert _count(body, "v_cvt_pk_fp8_f32") == 40
+    assert _count(body, "v_mov_b32_dpp") == 4            # the row maximum's DPP steps
+    assert _count(body, "v_add_f32_dpp") == 8            # mean and centred variance
+    assert _count(body, "v_permlane32_swap_b32_e32") == 3
+    assert _count(body, "global_store_dword") == 1       # the per-row scale
+    assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
+    assert not re.search(r"^\s+(flat|scratch)_", body, re.M)

@@ -372,3 +372,64 @@ def test_every_compiled_shape(rn, orc):
         gl = (FRAME, 5) if flags & rn.RN_GATE else None
         for rms in (False, True):
             _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, 2, 5, D)
+
+
+def test_hip_graph_capture_and_replay(rn, orc):
+    """The entry points can be captured in a HIP graph (torch.cuda.CUDAGraph):
+    three calls (fused, norm-only, FP8 output) captured once and replayed with
+    new input contents each time, each replay checked against the oracle, with
+    eager work and synchronisation between replays."""
+    import torch
+    B, L, D = 1, 48, 5120
+    shapes = {"x": (L, D), "residual": (L, D), "gate": (1, D), "scale": (1, D), "shift": (1, D)}
+    bufs = {k: torch.empty(s, dtype=torch.bfloat16, device="cuda") for k, s in shapes.items()}
+    y = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+    ro = torch.empty_like(y)
+    yn = torch.empty_like(y)
+    y8 = torch.empty((L, D), dtype=torch.float8_e4m3fn, device="cuda")
+    ys = torch.empty((L,), dtype=torch.float32, device="cuda")
+
+    def calls():
+        rn.resnorm_fused_fwd(y, ro, bufs["x"], bufs["residual"], bufs["gate"], None, None,
+                             bufs["scale"], bufs["shift"], B, L, D, rn.RN_GATE, (BCAST, 0),
+                             (BCAST, 0), 1e-6)
+        rn.norm_scale_shift_fwd(yn, ro, None, None, bufs["scale"], bufs["shift"], B, L, D, 0,
+                                (BCAST, 0), 1e-6)
+        rn.resnorm_fused_fwd_ex(y8, ro, bufs["x"], ro, bufs["gate"], None, None, bufs["scale"],
+                                bufs["shift"], B, L, D, rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6,
+                                y_dtype=rn.RN_DTYPE_FP8_E4M3, y_scale=ys)
+
+    def fill(seed):
+        inp = _small_problem(seed, True, False, (BCAST, 0), 0, (BCAST, 0), B, L, D)
+        for k in shapes:
+            bufs[k].copy_(to_dev(inp[k]))
+        return inp
+
+    fill(1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for seed in (11, 12, 13):
+        inp = fill(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_ref, ro_ref, _ = orc.fused(inp["x"], inp["residual"], inp["gate"], None, None,
+                                     inp["scale"], inp["shift"], B, L, D, False)
+        compare_outputs(to_host(y), y_ref, None, None, "graph replay %d y" % seed)
+        yn_ref, _ = orc.nss(ro_ref, None, None, inp["scale"], inp["shift"], B, L, D, False)
+        compare_outputs(to_host(yn), yn_ref, what="graph replay %d nss" % seed)
+        # the third call read residual_out in place of the residual (aliasing)
+        q, _, _, s8 = orc.fused(inp["x"], ro_ref, inp["gate"], None, None, inp["scale"],
+                                inp["shift"], B, L, D, False, y_dtype=2)
+        np.testing.assert_allclose(ys.cpu().numpy(), s8, rtol=2.0 ** -20)
+        same = np.mean(y8.view(torch.uint8).cpu().numpy() == q)
+        assert same > 0.999, same
+        # eager work between replays
+        torch.add(bufs["x"], 1.0).sum().item()
