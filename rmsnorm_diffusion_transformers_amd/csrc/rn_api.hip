@@ -121,10 +121,10 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
 }
 
 // The compiled shape for a problem (see kShapes); -1 if none covers D.
-int shape_for(int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
+int shape_for(int64_t R, int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
-  const bool many = streams >= 5 && D >= rn::kManyStreamsMinD;
+  const bool many = D >= rn::kManyStreamsMinD && (streams >= 5 || R <= rn::kSmallRows);
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
@@ -235,7 +235,7 @@ rn_status run(const Problem& p, void* stream) {
   if (st != RN_OK) return st;
   const int64_t R = p.B * p.L;
   if (R == 0) return RN_OK;
-  const int vi = shape_for(p.D, p.flags, p.fused, p.affine_dtype,
+  const int vi = shape_for(R, p.D, p.flags, p.fused, p.affine_dtype,
                            hbm_streams(p.flags, p.fused, p.gate_layout, p.ss_layout));
   rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
   if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
@@ -356,7 +356,7 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   if (!info) return fail(RN_EINVAL, "info is NULL");
   rn_status st = check_shape(B, L, D, flags, fused != 0);
   if (st != RN_OK) return st;
-  const int vi = shape_for(D, flags, fused != 0, RN_DTYPE_BF16,
+  const int vi = shape_for(B * L, D, flags, fused != 0, RN_DTYPE_BF16,
                            hbm_streams(flags, fused != 0, gate_layout, ss_layout));
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
   const rn::Shape s = rn::kShapes[vi];

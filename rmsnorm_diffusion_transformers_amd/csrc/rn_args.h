@@ -22,7 +22,10 @@ constexpr int kWaveSize = 64;
 //     loaded) <= kVgprBudget -- one wave per row at D = 5120;
 //   * a problem that also streams per-row scale/shift (or a per-row gate)
 //     runs best with 10 waves per row and 1-4 vectors per lane (shorter
-//     per-wave spans and more rows in flight), once D >= kManyStreamsMinD.
+//     per-wave spans and more rows in flight), once D >= kManyStreamsMinD;
+//   * so does a problem of at most kSmallRows rows, which is latency-bound:
+//     ten waves per row shorten each row's chain (L = 16, D = 5120: 5.6 us
+//     -> 2.9 us per call in a HIP graph).
 struct Shape {
   int w;
   int vpt;
@@ -33,6 +36,7 @@ constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1,
                              {2, 8, 2},  {2, 10, 2}, {4, 4, 1},  {4, 5, 1},  {4, 6, 1},
                              {4, 8, 1},  {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
 constexpr int kManyStreamsMinD = 2560;
+constexpr int kSmallRows = 512;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough

@@ -164,6 +164,8 @@ def test_describe_launch(rn):
     c3b = rn.describe_launch(1, 90000, 10240, rn.RN_GATE | rn.RN_RMS | rn.RN_WEIGHT)
     assert (c3b["waves_per_row"], c3b["vec_per_lane"], c3b["rows_per_block"]) == (4, 5, 1)
     c5 = rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True, (rn.RN_FRAME, 49), (rn.RN_FRAME, 49))
+    c1 = rn.describe_launch(1, 16, 5120, rn.RN_GATE, True)
+    assert (c1["waves_per_row"], c1["vec_per_lane"]) == (10, 1)
     assert (c5["waves_per_row"], c5["vec_per_lane"]) == (1, 10)
     small_row = rn.describe_launch(1, 8, 1024, rn.RN_GATE, True, (rn.RN_ROW, 0), (rn.RN_ROW, 0))
     assert small_row["waves_per_row"] == 1
@@ -171,10 +173,17 @@ def test_describe_launch(rn):
     assert (nss["waves_per_row"], nss["vec_per_lane"]) == (1, 10)
     assert rn.describe_launch(1, 3, 8, 0, False)["vec_per_lane"] == 1
     assert rn.describe_launch(1, 3, 1000, 0, False)["vec_per_lane"] == 2
-    big = rn.describe_launch(1, 3, 16384, 0, False)
+    big = rn.describe_launch(1, 3000, 16384, 0, False)
     assert (big["waves_per_row"], big["vec_per_lane"]) == (4, 8)
-    mid = rn.describe_launch(1, 3, 8192, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS, True)
+    mid = rn.describe_launch(1, 3000, 8192, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS, True)
     assert (mid["waves_per_row"], mid["vec_per_lane"]) == (4, 4)
+    # a few rows are latency-bound: ten waves per row from D = 2560 up
+    tiny = rn.describe_launch(1, 16, 5120, rn.RN_GATE, True)
+    assert (tiny["waves_per_row"], tiny["vec_per_lane"], tiny["grid_blocks"]) == (10, 1, 16)
+    assert rn.describe_launch(1, 3, 16384, 0, False)["vec_per_lane"] == 4
+    assert rn.describe_launch(1, 512, 5120, 0, False)["waves_per_row"] == 10
+    assert rn.describe_launch(1, 513, 5120, 0, False)["waves_per_row"] == 1
+    assert rn.describe_launch(1, 16, 2552, 0, False)["waves_per_row"] == 1
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
     for D in range(8, 16385, 8):
         for fused, flags, gl, sl in ((False, 0, (0, 0), (0, 0)), (True, 14, (1, 0), (1, 0))):

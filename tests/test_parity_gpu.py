@@ -343,17 +343,20 @@ def test_mean_offset_rows(rn, orc):
     compare_outputs(to_host(y), y_ref, what="mean offset 300")
 
 
+SHAPE_B, SHAPE_L = 2, 263   # 526 rows: above the small-problem threshold; a partial last workgroup
+
+
 def _shape_cases(rn):
     """One (D, fused, flags, scale/shift layout) per compiled (waves per row,
-    vectors per lane) shape."""
+    vectors per lane) shape, for a problem of SHAPE_B x SHAPE_L rows."""
     seen = {}
     flag_sets = [(False, 0), (True, rn.RN_GATE), (True, rn.RN_GATE | rn.RN_WEIGHT),
                  (True, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS), (False, rn.RN_WEIGHT | rn.RN_BIAS)]
     for D in range(8, 16385, 8):
         for fused, flags in flag_sets:
             for sl in ((BCAST, 0), (ROW, 0)):
-                gl = (FRAME, 5) if flags & rn.RN_GATE else (BCAST, 0)
-                i = rn.describe_launch(1, 1, D, flags, fused, gl, sl)
+                gl = (FRAME, 1) if flags & rn.RN_GATE else (BCAST, 0)
+                i = rn.describe_launch(SHAPE_B, SHAPE_L, D, flags, fused, gl, sl)
                 key = (i["waves_per_row"], i["vec_per_lane"])
                 if key not in seen:
                     seen[key] = (D, fused, flags, sl)
@@ -363,15 +366,15 @@ def _shape_cases(rn):
 def test_every_compiled_shape(rn, orc):
     """Every compiled (waves per row, vectors per lane) shape the planner can
     pick, at the first row width that selects it (a ragged row for most), with
-    B=2, L=5 (so the last workgroup of a multi-row shape is partly empty)."""
+    B=2, L=263 (so the last workgroup of a four-row shape is partly empty)."""
     cases = _shape_cases(rn)
     assert len(cases) == 20, sorted(cases)
     for (w, vpt), (D, fused, flags, sl) in sorted(cases.items()):
         log("shape W=%d VPT=%d via D=%d fused=%s flags=%d ss=%s" % (w, vpt, D, fused, flags, sl))
         aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
-        gl = (FRAME, 5) if flags & rn.RN_GATE else None
+        gl = (FRAME, 1) if flags & rn.RN_GATE else None
         for rms in (False, True):
-            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, 2, 5, D)
+            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, SHAPE_B, SHAPE_L, D)
 
 
 def test_hip_graph_capture_and_replay(rn, orc):
