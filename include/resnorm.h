@@ -169,7 +169,10 @@ const char* rn_last_error(void);
  * waves per activation row, waves and rows per workgroup, workgroup size and
  * grid size.  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
  * (0); the layouts matter because per-row modulation operands add HBM
- * streams, which changes the preferred shape. */
+ * streams, which changes the preferred shape, and so does the row count
+ * (problems of at most 512 rows are latency-bound).  The answer is for bf16
+ * weight/bias; binary32 weight/bias (the _ex entry points) hold twice the
+ * registers per vector and may get a shorter per-wave span. */
 typedef struct {
   int32_t vec_per_lane;
   int32_t waves_per_row;
