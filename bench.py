@@ -101,7 +101,25 @@ def time_calls(fn, steps, warmup):
     return start.elapsed_time(end) / steps, time.perf_counter() - w0
 
 
-def time_workload(rn, wl, steps, warmup, dev, keep=False):
+def launch_stats(fn, steps):
+    """Per-launch durations (ms) of `steps` calls, each between its own pair of
+    events on the current stream: median, min, max.  Run after the timed
+    region, so that the extra events do not perturb it."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"median": round(ts[len(ts) // 2], 5), "min": round(ts[0], 5), "max": round(ts[-1], 5),
+            "n": len(ts)}
+
+
+def time_workload(rn, wl, steps, warmup, dev, keep=False, stats=False):
     import torch
 
     import synth
@@ -114,12 +132,14 @@ def time_workload(rn, wl, steps, warmup, dev, keep=False):
     y = torch.empty_like(d["x"])
     ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
     stream = torch.cuda.current_stream()
-    ms, wall = time_calls(lambda: launch_workload(rn, wl, d, y, ro, stream), steps, warmup)
+    call = lambda: launch_workload(rn, wl, d, y, ro, stream)  # noqa: E731
+    ms, wall = time_calls(call, steps, warmup)
+    per_launch = launch_stats(call, steps) if stats else None
     if keep:
-        return ms, wall, (d, y, ro)
+        return ms, wall, per_launch, (d, y, ro)
     del d, y, ro
     torch.cuda.empty_cache()
-    return ms, wall
+    return ms, wall, per_launch
 
 
 def extras(rn, dev_tensors, steps, warmup):
@@ -300,25 +320,33 @@ def calibrate(steps, warmup, dev):
 
 
 def cpu_baseline(wl):
-    """The oracle (as it is) on a bounded sample of the same workload, on this
-    host's cores.  Returns the record for the JSON line."""
-    import synth
+    """The oracle (as it is) on this host's cores: every row of the workload on
+    all threads (up to 16), and the first 16384 rows on one thread.  Input
+    generation is not timed.  Returns the record for the JSON line."""
     import oracle
-    rows = 32768
     n = threads()
-    rows = min(rows, wl.R)
+    rows = wl.R
     t0 = time.time()
     inp = _first_rows(wl, rows, n)
     log("cpu baseline: inputs for %d rows in %.1f s" % (rows, time.time() - t0))
     o = oracle.Oracle()
+    per_row = wl.algorithmic_bytes() / wl.R
     t0 = time.perf_counter()
     o.run_workload(wl, inp, row0=0, nrows=rows, threads=n)
     dt = time.perf_counter() - t0
-    per_row = wl.algorithmic_bytes() / wl.R
+    log("cpu baseline: %d rows on %d threads in %.2f s" % (rows, n, dt))
+    rows1 = min(16384, wl.R)
+    t1 = time.perf_counter()
+    o.run_workload(wl, inp, row0=0, nrows=rows1, threads=1)
+    dt1 = time.perf_counter() - t1
+    log("cpu baseline: %d rows on 1 thread in %.2f s" % (rows1, dt1))
     return {"value": round(rows * per_row / dt / 1e9, 3), "unit": "GB/s", "cores": n,
             "kind": "oracle", "rows_per_s": round(rows / dt, 1),
-            "sample": "first %d of %d rows of %s (all operands they read), oracle threads=%d, "
-                      "%.2f s wall" % (rows, wl.R, wl.name, n, dt)}
+            "sample": "all %d rows of %s (every operand), oracle threads=%d, %.2f s wall; "
+                      "input generation not timed" % (rows, wl.name, n, dt),
+            "single_thread": {"value": round(rows1 * per_row / dt1 / 1e9, 3), "unit": "GB/s",
+                              "rows_per_s": round(rows1 / dt1, 1),
+                              "sample": "first %d rows, 1 thread, %.2f s wall" % (rows1, dt1)}}
 
 
 def _first_rows(wl, rows, n):
@@ -371,12 +399,13 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     want_extras = not args.no_extras and args.workload == HEADLINE
     if want_extras:
-        ms, wall, kept = time_workload(rn, wl, args.steps, args.warmup, dev, keep=True)
+        ms, wall, per_launch, kept = time_workload(rn, wl, args.steps, args.warmup, dev,
+                                                   keep=True, stats=True)
         variants, mix = extras(rn, kept, args.steps, args.warmup)
         del kept
         torch.cuda.empty_cache()
     else:
-        ms, wall = time_workload(rn, wl, args.steps, args.warmup, dev)
+        ms, wall, per_launch = time_workload(rn, wl, args.steps, args.warmup, dev, stats=True)
     nbytes = wl.algorithmic_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("%s: %.4f ms/launch, %.1f GB/s (%.1f%% of %g)" % (wl.name, ms, gbs, 100 * gbs / HBM_PEAK_GBS,
@@ -384,13 +413,13 @@ def main():
     companions = []
     if not args.no_companion and args.workload == HEADLINE:
         wc = synth.WORKLOADS[COMPANION]
-        cms, _ = time_workload(rn, wc, args.steps, args.warmup, dev)
+        cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True)
         cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
         log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
         companions.append({"workload": wc.name, "ms_per_launch": round(cms, 5),
                            "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
                            "algorithmic_bytes": wc.algorithmic_bytes(),
-                           "traffic": measured_traffic(wc.name)})
+                           "traffic": measured_traffic(wc.name), "launch_ms": cstats})
     info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused",
                               wl.gate_layout or (0, 0), wl.ss_layout)
     ref = copy_reference(args.steps, args.warmup, dev)
@@ -415,6 +444,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)},
         "wall_s_timed_region": round(wall, 4),
+        "launch_ms": per_launch,
         "companions": companions,
         "copy_reference": ref,
     }
