@@ -121,16 +121,36 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
 }
 
 // The compiled shape for a problem (see kShapes); -1 if none covers D.
+// Waves per row the planner aims for (0: the first compiled shape with W < 10
+// that fits the register budget); the measurements behind each rule are
+// listed with the shape table.
+int preferred_waves(int64_t R, int64_t D, int streams) {
+  if (D >= rn::kManyStreamsMinD && streams >= 5) return 10;
+  if (D < rn::kSplitMinD) return 0;
+  if (R <= rn::kTinyRows && D > 4096 && D <= 5120) return 10;
+  if (R <= rn::kSmallRows) return 4;
+  if (R <= rn::kMidRowsSplit4 && (D >= rn::kManyStreamsMinD || R <= 2 * rn::kSmallRows))
+    return D <= 3072 ? 2 : 4;
+  if (R <= rn::kMidRows && D >= rn::kManyStreamsMinD) return 2;
+  return 0;
+}
+
 int shape_for(int64_t R, int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
-  const bool many = D >= rn::kManyStreamsMinD && (streams >= 5 || R <= rn::kSmallRows);
+  const int want = preferred_waves(R, D, streams);
+  auto covers = [&](const rn::Shape& s) { return (int64_t)rn::kWaveSize * s.w * s.vpt >= nvec; };
+  if (want != 0) {
+    for (int i = 0; i < rn::kNumShapes; ++i) {
+      const rn::Shape s = rn::kShapes[i];
+      if (s.w == want && covers(s) && (want == 10 || s.vpt * ops <= rn::kVgprBudget)) return i;
+    }
+  }
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
-    if ((int64_t)rn::kWaveSize * s.w * s.vpt < nvec) continue;
-    if ((s.w == 10) != many) continue;
-    if (many || s.vpt * ops <= rn::kVgprBudget) return i;
+    if (s.w == 10 || !covers(s)) continue;
+    if (s.vpt * ops <= rn::kVgprBudget) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
   return fallback;

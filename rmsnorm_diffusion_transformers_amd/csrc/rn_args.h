@@ -14,29 +14,43 @@ constexpr int kWaveSize = 64;
 // covers rows of up to 64 * W * VPT vectors (D = 512 * W * VPT); tail lanes of
 // shorter rows are masked.
 //
-// Choice (measured on MI355X at L = 90000-176400):
+// Choice (measured on MI355X; each rule from sweeps over every compiled shape):
 //   * a problem that streams at most 4 tensors through HBM (x, y, and the
 //     residual pair of the fused op; broadcast / per-frame modulation rows
-//     come from L2) runs best with long per-wave rows: the first shape with
-//     W < 10, in this order, that covers D and keeps VPT * (row operands
-//     loaded) <= kVgprBudget -- one wave per row at D = 5120;
+//     come from L2) and has more than kMidRows rows runs best with long
+//     per-wave rows: the first shape with W < 10, in table order, that
+//     covers D and keeps VPT * (row operands loaded) <= kVgprBudget -- one
+//     wave per row at D = 5120 (L = 90000-176400);
 //   * a problem that also streams per-row scale/shift (or a per-row gate)
 //     runs best with 10 waves per row and 1-4 vectors per lane (shorter
 //     per-wave spans and more rows in flight), once D >= kManyStreamsMinD;
-//   * so does a problem of at most kSmallRows rows, which is latency-bound:
-//     ten waves per row shorten each row's chain (L = 16, D = 5120: 5.6 us
-//     -> 2.9 us per call in a HIP graph).
+//   * from D >= kSplitMinD, problems of a few hundred rows leave most SIMDs
+//     idle with one wave per row and are bound by each row's load -> reduce
+//     -> store chain, so the row is split so that each wave holds 2-5
+//     vectors per lane: 4 waves per row up to kSmallRows rows, then 2 waves
+//     while D <= 3072 and 4 above, up to kMidRowsSplit4 rows (up to 2 *
+//     kSmallRows below D = 2560), then 2 up to kMidRows (from D >= 2560);
+//     the sweep at 64-4096 rows found these 10-30 % faster than one wave per
+//     row (e.g. 512 rows, D = 5120: 6.3 -> 5.3 us);
+//   * at most kTinyRows rows with 4096 < D <= 5120 use 10 waves of one
+//     vector each (L = 16, D = 5120: 2.8 us per call in a HIP graph).
 struct Shape {
   int w;
   int vpt;
   int rpb;
 };
+// Sorted by W, then VPT: the planner takes the first fit of a given W.
 constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1, 5, 4},
-                             {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 5, 2},  {2, 6, 2},
-                             {2, 8, 2},  {2, 10, 2}, {4, 4, 1},  {4, 5, 1},  {4, 6, 1},
-                             {4, 8, 1},  {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
+                             {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 3, 2},  {2, 4, 2},
+                             {2, 5, 2},  {2, 6, 2},  {2, 8, 2},  {2, 10, 2}, {4, 2, 1},
+                             {4, 3, 1},  {4, 4, 1},  {4, 5, 1},  {4, 6, 1},  {4, 8, 1},
+                             {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
 constexpr int kManyStreamsMinD = 2560;
-constexpr int kSmallRows = 512;
+constexpr int kSplitMinD = 2048;
+constexpr int kTinyRows = 128;
+constexpr int kSmallRows = 256;
+constexpr int kMidRowsSplit4 = 768;
+constexpr int kMidRows = 1536;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough

@@ -426,14 +426,15 @@ KernelFn kernel_for_shape(int shape) {
     return row_kernel<OP, i>;
     RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
     RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
-    RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18) RN_CASE(19)
+    RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18) RN_CASE(19) RN_CASE(20) RN_CASE(21)
+    RN_CASE(22) RN_CASE(23)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumShapes == 20, "kernel_for_shape lists every shape");
+static_assert(kNumShapes == 24, "kernel_for_shape lists every shape");
 
 // Table of one (norm, op, gate, output) family over the affine variants.
 template <bool RMS, bool FUSED, bool GATE, int OUT>

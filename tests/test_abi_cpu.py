@@ -150,9 +150,16 @@ def test_status_mapping_in_binding(rn):
     assert e.value.status == rn.RN_EINVAL and "multiple of 8" in str(e.value)
 
 
+def plan_of(rn, R, D):
+    i = rn.describe_launch(1, R, D, 0, False)
+    return i["waves_per_row"], i["vec_per_lane"]
+
+
 def test_describe_launch(rn):
-    """The planner: smallest waves-per-row that covers D within the register
-    budget (vectors per lane x row operands <= 52)."""
+    """The planner: for large problems the smallest waves-per-row that covers
+    D within the register budget (vectors per lane x row operands <= 52); for
+    a few hundred rows, rows split over 2-10 waves; ten waves when per-row
+    modulation adds HBM streams."""
     info = rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True)
     assert (info["waves_per_row"], info["vec_per_lane"]) == (1, 10)
     assert info["block_threads"] == 256 and info["rows_per_block"] == 4
@@ -177,13 +184,22 @@ def test_describe_launch(rn):
     assert (big["waves_per_row"], big["vec_per_lane"]) == (4, 8)
     mid = rn.describe_launch(1, 3000, 8192, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS, True)
     assert (mid["waves_per_row"], mid["vec_per_lane"]) == (4, 4)
-    # a few rows are latency-bound: ten waves per row from D = 2560 up
+    # a few rows are latency-bound: ten one-vector waves for D in (4096, 5120]
     tiny = rn.describe_launch(1, 16, 5120, rn.RN_GATE, True)
     assert (tiny["waves_per_row"], tiny["vec_per_lane"], tiny["grid_blocks"]) == (10, 1, 16)
-    assert rn.describe_launch(1, 3, 16384, 0, False)["vec_per_lane"] == 4
-    assert rn.describe_launch(1, 512, 5120, 0, False)["waves_per_row"] == 10
-    assert rn.describe_launch(1, 513, 5120, 0, False)["waves_per_row"] == 1
-    assert rn.describe_launch(1, 16, 2552, 0, False)["waves_per_row"] == 1
+    assert plan_of(rn, 3, 16384) == (4, 8)
+    assert rn.describe_launch(1, 128, 5120, 0, False)["waves_per_row"] == 10
+    # a few hundred rows: rows split so that each wave holds 2-5 vectors per lane
+    plan = lambda R, D: plan_of(rn, R, D)  # noqa: E731
+    assert plan(129, 5120) == (4, 3)
+    assert plan(256, 2048) == (4, 2) and plan(256, 10240) == (4, 5)
+    assert plan(257, 3072) == (2, 3) and plan(768, 3072) == (2, 3)
+    assert plan(512, 2048) == (2, 3) and plan(513, 2048) == (1, 4)
+    assert plan(768, 5120) == (4, 3) and plan(769, 5120) == (2, 5)
+    assert plan(1536, 4096) == (2, 4) and plan(1537, 4096) == (1, 8)
+    assert plan(1536, 2048) == (1, 4) and plan(1000, 2040) == (1, 4)
+    assert plan(100, 2040) == (1, 4)
+    assert plan(16, 2552) == (4, 2)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
     for D in range(8, 16385, 8):
         for fused, flags, gl, sl in ((False, 0, (0, 0), (0, 0)), (True, 14, (1, 0), (1, 0))):

@@ -343,38 +343,43 @@ def test_mean_offset_rows(rn, orc):
     compare_outputs(to_host(y), y_ref, what="mean offset 300")
 
 
-SHAPE_B, SHAPE_L = 2, 263   # 526 rows: above the small-problem threshold; a partial last workgroup
+
+
+SHAPE_ROWS = ((2, 263), (2, 600), (2, 1031))   # a few hundred rows, a mid-size and a large problem
 
 
 def _shape_cases(rn):
-    """One (D, fused, flags, scale/shift layout) per compiled (waves per row,
-    vectors per lane) shape, for a problem of SHAPE_B x SHAPE_L rows."""
+    """One (B, L, D, fused, flags, scale/shift layout) per compiled (waves per
+    row, vectors per lane) shape, at the first row count and row width that
+    select it."""
     seen = {}
     flag_sets = [(False, 0), (True, rn.RN_GATE), (True, rn.RN_GATE | rn.RN_WEIGHT),
                  (True, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS), (False, rn.RN_WEIGHT | rn.RN_BIAS)]
-    for D in range(8, 16385, 8):
-        for fused, flags in flag_sets:
-            for sl in ((BCAST, 0), (ROW, 0)):
-                gl = (FRAME, 1) if flags & rn.RN_GATE else (BCAST, 0)
-                i = rn.describe_launch(SHAPE_B, SHAPE_L, D, flags, fused, gl, sl)
-                key = (i["waves_per_row"], i["vec_per_lane"])
-                if key not in seen:
-                    seen[key] = (D, fused, flags, sl)
+    for B, L in SHAPE_ROWS:
+        for D in range(8, 16385, 8):
+            for fused, flags in flag_sets:
+                for sl in ((BCAST, 0), (ROW, 0)):
+                    gl = (FRAME, 1) if flags & rn.RN_GATE else (BCAST, 0)
+                    i = rn.describe_launch(B, L, D, flags, fused, gl, sl)
+                    key = (i["waves_per_row"], i["vec_per_lane"])
+                    if key not in seen:
+                        seen[key] = (B, L, D, fused, flags, sl)
     return seen
 
 
 def test_every_compiled_shape(rn, orc):
     """Every compiled (waves per row, vectors per lane) shape the planner can
     pick, at the first row width that selects it (a ragged row for most), with
-    B=2, L=263 (so the last workgroup of a four-row shape is partly empty)."""
+    odd L (so the last workgroup of a multi-row shape is partly empty)."""
     cases = _shape_cases(rn)
-    assert len(cases) == 20, sorted(cases)
-    for (w, vpt), (D, fused, flags, sl) in sorted(cases.items()):
-        log("shape W=%d VPT=%d via D=%d fused=%s flags=%d ss=%s" % (w, vpt, D, fused, flags, sl))
+    assert len(cases) == 24, sorted(cases)
+    for (w, vpt), (B, L, D, fused, flags, sl) in sorted(cases.items()):
+        log("shape W=%d VPT=%d via B=%d L=%d D=%d fused=%s flags=%d ss=%s" % (w, vpt, B, L, D, fused,
+                                                                            flags, sl))
         aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
         gl = (FRAME, 1) if flags & rn.RN_GATE else None
         for rms in (False, True):
-            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, SHAPE_B, SHAPE_L, D)
+            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, B, L, D)
 
 
 def test_hip_graph_capture_and_replay(rn, orc):
