@@ -101,7 +101,7 @@ def _problem(seed, fused, gate_layout, aff, ss_layout, B, L, D):
     return inp
 
 
-def _run(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype):
+def _run(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype, eps=1e-6):
     """One problem through the _ex entry point and the oracle; checks and
     returns a short statistic."""
     inp = _problem(seed, fused, gate_layout, aff, ss_layout, B, L, D)
@@ -115,8 +115,8 @@ def _run(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtyp
     ydt = {0: torch.bfloat16, 1: torch.float32, 2: torch.float8_e4m3fn}[y_dtype]
     y = torch.empty((R, D), dtype=ydt, device="cuda")
     ys = torch.empty((R,), dtype=torch.float32, device="cuda") if y_dtype == 2 else None
-    case = "seed=%d fused=%s rms=%s gate=%s aff=%d ss=%s B=%d L=%d D=%d y=%d" % (
-        seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype)
+    case = "seed=%d fused=%s rms=%s gate=%s aff=%d ss=%s B=%d L=%d D=%d y=%d eps=%g" % (
+        seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype, eps)
     adt = rn.RN_DTYPE_F32 if aff32 else rn.RN_DTYPE_BF16
     if fused:
         if gate_layout is not None:
@@ -124,20 +124,20 @@ def _run(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtyp
         ro = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
         rn.resnorm_fused_fwd_ex(y, ro, d["x"], d["residual"], d.get("gate"), d.get("weight"),
                                 d.get("bias"), d["scale"], d["shift"], B, L, D, flags,
-                                gate_layout or (BCAST, 0), ss_layout, 1e-6, adt, y_dtype, ys)
+                                gate_layout or (BCAST, 0), ss_layout, eps, adt, y_dtype, ys)
         torch.cuda.synchronize()
         res = orc.fused(inp["x"], inp["residual"], inp.get("gate"), inp.get("weight"),
                         inp.get("bias"), inp["scale"], inp["shift"], B, L, D, rms,
-                        gate_layout or (BCAST, 0), ss_layout, 1e-6, affine_f32=aff32,
+                        gate_layout or (BCAST, 0), ss_layout, eps, affine_f32=aff32,
                         y_dtype=y_dtype, threads=THREADS)
         y_ref, ro_ref = res[0], res[1]
         assert np.array_equal(to_host(ro), ro_ref), case + ": residual_out not bit-exact"
     else:
         rn.norm_scale_shift_fwd_ex(y, d["x"], d.get("weight"), d.get("bias"), d["scale"],
-                                   d["shift"], B, L, D, flags, ss_layout, 1e-6, adt, y_dtype, ys)
+                                   d["shift"], B, L, D, flags, ss_layout, eps, adt, y_dtype, ys)
         torch.cuda.synchronize()
         res = orc.nss(inp["x"], inp.get("weight"), inp.get("bias"), inp["scale"], inp["shift"],
-                      B, L, D, rms, ss_layout, 1e-6, affine_f32=aff32, y_dtype=y_dtype,
+                      B, L, D, rms, ss_layout, eps, affine_f32=aff32, y_dtype=y_dtype,
                       threads=THREADS)
         y_ref = res[0]
     if y_dtype == 0:
@@ -177,6 +177,50 @@ def test_output_dtypes_matrix(rn, orc, D, y_dtype):
                 gl = (ROW, 0) if fused and k % 2 else ((BCAST, 0) if fused else None)
                 _run(rn, orc, 700 + k + D, fused, rms, gl, aff, sl, 2, 6, D, y_dtype)
                 k += 1
+
+
+def _random_cases(n, seed):
+    """n seeded random problems: row widths spread over 8..16384 (half of them
+    within 8 elements of a multiple of 512, where shapes change), 1..~3000
+    rows, every flag, layout, affine type, output type, and four eps values."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        if rng.random() < 0.5:
+            D = int(rng.integers(1, 2049)) * 8
+        else:
+            D = int(np.clip(512 * int(rng.integers(1, 33)) + 8 * int(rng.integers(-1, 2)), 8, 16384))
+        B = int(rng.integers(1, 4))
+        F = int(rng.choice([1, 2, 3, 5]))
+        L = F * max(1, int(np.exp(rng.uniform(0, np.log(1000))) / F))
+        if B * L * D > 8_000_000:
+            continue
+        fused = bool(rng.random() < 0.6)
+        lay = lambda: [(BCAST, 0), (ROW, 0), (FRAME, F)][int(rng.integers(0, 3))]  # noqa: E731
+        gl = (lay() if rng.random() < 0.75 else None) if fused else None
+        cases.append(dict(fused=fused, rms=bool(rng.random() < 0.5), gate_layout=gl,
+                          aff=int(rng.integers(0, 5)), ss_layout=lay(), B=B, L=L, D=D,
+                          y_dtype=int(rng.choice([0, 0, 0, 1, 2])),
+                          eps=float(rng.choice([1e-6, 1e-5, 0.0, 1e-2]))))
+    return cases
+
+
+def test_random_matrix(rn, orc):
+    """120 seeded random problems through the _ex entry points against the
+    oracle, each at the bar of its output type; the planner picks whatever
+    shape each problem gets (all four waves-per-row families are exercised)."""
+    cases = _random_cases(120, 4321)
+    seen = set()
+    for k, c in enumerate(cases):
+        flags = (rn.RN_RMS if c["rms"] else 0) | (rn.RN_WEIGHT if c["aff"] else 0) | \
+            (rn.RN_BIAS if c["aff"] in (2, 4) else 0) | (rn.RN_GATE if c["gate_layout"] else 0)
+        info = rn.describe_launch(c["B"], c["L"], c["D"], flags, c["fused"],
+                                  c["gate_layout"] or (BCAST, 0), c["ss_layout"])
+        seen.add(info["waves_per_row"])
+        log("random case %d: %s" % (k, c))
+        _run(rn, orc, 1000 + k, c["fused"], c["rms"], c["gate_layout"], c["aff"], c["ss_layout"],
+             c["B"], c["L"], c["D"], c["y_dtype"], c["eps"])
+    assert seen == {1, 2, 4, 10}, seen
 
 
 @pytest.mark.parametrize("B", [2, 4])
