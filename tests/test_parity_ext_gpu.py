@@ -317,3 +317,67 @@ def test_full_size_ext(rn, orc, y_dtype, aff):
         same = check_y_fp8(y.view(torch.uint8).cpu().numpy(), ys.cpu().numpy(), res[0], res[3],
                            "full fp8")
         log("full size fp8 y: %.4f%% codes identical" % (100 * same))
+
+
+def test_tensors_over_4gib(rn, orc):
+    """Activations larger than 4 GiB (B 1, L 540677, D 4096: 4.4 GB per bf16
+    tensor, 8.9 GB for a binary32 y), so byte offsets pass 2^32 both in the
+    bf16 tensors (from row 524288) and in the binary32 output (from row
+    262144): the rows on either side of each boundary, the first and the last
+    rows, against the oracle (residual_out bit-exact, y at its bar)."""
+    B, L, D = 1, 540677, 4096
+    R = B * L
+    wid = 77
+    specs = {"x": synth.TensorSpec(synth.X, synth.NORMAL, 0.0, 1.0),
+             "residual": synth.TensorSpec(synth.RES, synth.NORMAL, 0.0, 1.0)}
+    mod = {"gate": synth.fill(synth.TensorSpec(synth.GATE, synth.UNIFORM, 0.0, 1.0), wid, D),
+           "scale": synth.fill(synth.TensorSpec(synth.SCALE, synth.NORMAL, 0.0, 0.1), wid, D),
+           "shift": synth.fill(synth.TensorSpec(synth.SHIFT, synth.NORMAL, 0.0, 0.1), wid, D)}
+    log("over 4 GiB: generating %d x %d inputs" % (R, D))
+    dev = {}
+    for k, spec in specs.items():
+        t = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+        for a in range(0, R, 65536):
+            b = min(R, a + 65536)
+            host = synth.fill(spec, wid, (b - a) * D, idx0=a * D, threads=THREADS)
+            t[a:b].copy_(torch.from_numpy(host.view(np.int16)).view(torch.bfloat16).view(b - a, D))
+        dev[k] = t
+    dm = {k: to_dev(v.reshape(1, D)) for k, v in mod.items()}
+    ro = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+    assert ro.numel() * 2 > 2 ** 32
+    args = (dev["x"], dev["residual"], dm["gate"], None, None, dm["scale"], dm["shift"], B, L, D,
+            rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6)
+    log("over 4 GiB: bf16 y")
+    rn.resnorm_fused_fwd(y, ro, *args)
+    torch.cuda.synchronize()
+
+    def rows_of(t, r0, n):
+        return t[r0:r0 + n].contiguous()
+
+    def oracle_rows(r0, n, y_dtype):
+        xs = synth.fill(specs["x"], wid, n * D, idx0=r0 * D).reshape(n, D)
+        rs = synth.fill(specs["residual"], wid, n * D, idx0=r0 * D).reshape(n, D)
+        return orc.fused(xs, rs, mod["gate"].reshape(1, D), None, None, mod["scale"].reshape(1, D),
+                         mod["shift"].reshape(1, D), B, L, D, False, (BCAST, 0), (BCAST, 0), 1e-6,
+                         row0=r0, nrows=n, y_dtype=y_dtype)
+
+    samples = [0, 262144 - 64, 524288 - 64, R - 64]
+    for r0 in samples:
+        y_ref, ro_ref, _ = oracle_rows(r0, 128 if r0 != R - 64 else 64, 0)
+        n = y_ref.shape[0]
+        compare_outputs(to_host(rows_of(y, r0, n)), y_ref, to_host(rows_of(ro, r0, n)), ro_ref,
+                        "over 4 GiB, rows %d..%d" % (r0, r0 + n))
+    del y
+    log("over 4 GiB: binary32 y")
+    y32 = torch.empty((R, D), dtype=torch.float32, device="cuda")
+    ro.zero_()
+    rn.resnorm_fused_fwd_ex(y32, ro, *args, rn.RN_DTYPE_BF16, rn.RN_DTYPE_F32)
+    torch.cuda.synchronize()
+    for r0 in samples:
+        y_ref, ro_ref, _ = oracle_rows(r0, 128 if r0 != R - 64 else 64, 1)
+        n = y_ref.shape[0]
+        assert np.array_equal(to_host(rows_of(ro, r0, n)), ro_ref), r0
+        check_y_f32(rows_of(y32, r0, n).cpu().numpy(), y_ref, "over 4 GiB f32, rows %d" % r0)
+    del y32, ro, dev
+    torch.cuda.empty_cache()
