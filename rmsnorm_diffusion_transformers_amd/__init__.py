@@ -137,10 +137,39 @@ def _dtype_code(dt) -> int:
     raise TypeError("unsupported element type %s" % dt)
 
 
-def _stream(stream):
+def _rows(lay, B: int, L: int) -> int:
+    kind, frames = (lay.kind, lay.frames) if isinstance(lay, rn_layout) else lay
+    return {RN_BCAST: 1, RN_ROW: B * L, RN_FRAME: B * frames}.get(int(kind), 0)
+
+
+def _check_tensors(named):
+    """Host-side checks of the tensors an entry point receives (int addresses
+    are passed through unchecked): one common device, and at least as many
+    elements as the sizes and layouts make the kernel touch.  `named` is a
+    sequence of (name, tensor or address or None, elements needed).  Returns
+    the device index (None when only addresses were given)."""
+    import torch
+    Tensor = torch.Tensor
+    dev = first = None
+    for name, t, need in named:
+        if not isinstance(t, Tensor):
+            continue
+        if t.numel() < need:
+            raise ValueError("%s has %d elements; the sizes and layout need %d" % (name, t.numel(), need))
+        d = t.get_device()   # GPU index; -1 for host and meta tensors
+        if first is None:
+            dev, first = d, t
+        elif d != dev or (d < 0 and t.device != first.device):
+            raise ValueError("%s is on %s but other operands are on %s" % (name, t.device, first.device))
+    return dev if dev is not None and dev >= 0 else None
+
+
+def _stream(stream, device=None):
+    """The stream to enqueue on: the given one, else torch's current stream of
+    the operands' device."""
     if stream is None:
         import torch
-        return torch.cuda.current_stream().cuda_stream
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -157,20 +186,40 @@ def resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, s
                       flags, gate_layout=(RN_BCAST, 0), ss_layout=(RN_BCAST, 0), eps=1e-6,
                       stream=None) -> None:
     """Enqueue the fused op (C entry point of the same name); raises RnError."""
+    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                        gate_layout, ss_layout, None)
     _check(_lib.resnorm_fused_fwd(_addr(y), _addr(residual_out), _addr(x), _addr(residual),
                                   _addr(gate), _addr(weight), _addr(bias), _addr(scale),
                                   _addr(shift), int(B), int(L), int(D), int(flags),
                                   _layout(gate_layout), _layout(ss_layout), float(eps),
-                                  _stream(stream)))
+                                  _stream(stream, dev)))
+
+
+def _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                  gate_layout, ss_layout, y_scale):
+    B, L, D = int(B), int(L), int(D)
+    n, ss = B * L * D, _rows(ss_layout, B, L) * D
+    return _check_tensors((("y", y, n), ("residual_out", residual_out, n), ("x", x, n),
+                           ("residual", residual, n), ("gate", gate, _rows(gate_layout, B, L) * D),
+                           ("weight", weight, D), ("bias", bias, D), ("scale", scale, ss),
+                           ("shift", shift, ss), ("y_scale", y_scale, B * L)))
+
+
+def _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale):
+    B, L, D = int(B), int(L), int(D)
+    n, ss = B * L * D, _rows(ss_layout, B, L) * D
+    return _check_tensors((("y", y, n), ("x", x, n), ("weight", weight, D), ("bias", bias, D),
+                           ("scale", scale, ss), ("shift", shift, ss), ("y_scale", y_scale, B * L)))
 
 
 def norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
                          ss_layout=(RN_BCAST, 0), eps=1e-6, stream=None) -> None:
     """Enqueue the norm-only op (C entry point of the same name); raises RnError."""
+    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, None)
     _check(_lib.norm_scale_shift_fwd(_addr(y), _addr(x), _addr(weight), _addr(bias),
                                      _addr(scale), _addr(shift), int(B), int(L), int(D),
                                      int(flags), _layout(ss_layout), float(eps),
-                                     _stream(stream)))
+                                     _stream(stream, dev)))
 
 
 def resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L,
@@ -180,13 +229,15 @@ def resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale
     """Enqueue the fused op with other element types (C entry point of the same
     name): binary32 weight/bias; binary32 or FP8 E4M3 y (FP8 with per-row
     binary32 scales in y_scale)."""
+    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                        gate_layout, ss_layout, y_scale)
     ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
     _check(_lib.resnorm_fused_fwd_ex(_addr(y, y_dtype), _addr(residual_out), _addr(x),
                                      _addr(residual), _addr(gate),
                                      _addr(weight, affine_dtype), _addr(bias, affine_dtype),
                                      _addr(scale), _addr(shift), int(B), int(L), int(D),
                                      int(flags), _layout(gate_layout), _layout(ss_layout),
-                                     float(eps), ctypes.byref(ext), _stream(stream)))
+                                     float(eps), ctypes.byref(ext), _stream(stream, dev)))
 
 
 def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
@@ -194,11 +245,12 @@ def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
                             y_dtype=RN_DTYPE_BF16, y_scale=None, stream=None) -> None:
     """Enqueue the norm-only op with other element types (C entry point of the
     same name)."""
+    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale)
     ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
     _check(_lib.norm_scale_shift_fwd_ex(_addr(y, y_dtype), _addr(x), _addr(weight, affine_dtype),
                                         _addr(bias, affine_dtype), _addr(scale), _addr(shift),
                                         int(B), int(L), int(D), int(flags), _layout(ss_layout),
-                                        float(eps), ctypes.byref(ext), _stream(stream)))
+                                        float(eps), ctypes.byref(ext), _stream(stream, dev)))
 
 
 def describe_launch(B, L, D, flags, fused=True, gate_layout=(RN_BCAST, 0),

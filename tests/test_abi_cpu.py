@@ -233,6 +233,36 @@ def test_no_cpu_path(rn):
                             torch.zeros(8, dtype=torch.bfloat16), "layer", 1e-6, stream=0)
 
 
+def test_binding_checks_tensor_sizes_and_devices(rn):
+    """The tensor wrappers refuse tensors smaller than the sizes and layouts
+    make the kernel touch, and operands on different devices, before any
+    library call (CPU tensors: the checks run first, no GPU needed)."""
+    import torch
+    bf = dict(dtype=torch.bfloat16)
+    x = torch.zeros(2 * 3 * 8, **bf)
+    small = torch.zeros(2 * 3 * 8 - 1, **bf)
+    row = torch.zeros(8, **bf)
+    with pytest.raises(ValueError, match="y has 47 elements"):
+        rn.norm_scale_shift_fwd(small, x, None, None, row, row, 2, 3, 8, 0, stream=0)
+    with pytest.raises(ValueError, match="scale has 8 elements; the sizes and layout need 48"):
+        rn.norm_scale_shift_fwd(x, x, None, None, row, row, 2, 3, 8, 0, (rn.RN_ROW, 0), stream=0)
+    with pytest.raises(ValueError, match="gate has 8 elements; the sizes and layout need 48"):
+        rn.resnorm_fused_fwd(x, x.clone(), x, x.clone(), row, None, None, row, row, 2, 3, 8,
+                             rn.RN_GATE, (rn.RN_FRAME, 3), (rn.RN_BCAST, 0), stream=0)
+    with pytest.raises(ValueError, match="y_scale has 5 elements"):
+        rn.norm_scale_shift_fwd_ex(torch.zeros(48, dtype=torch.float8_e4m3fn), x, None, None, row,
+                                   row, 2, 3, 8, 0, y_dtype=rn.RN_DTYPE_FP8_E4M3,
+                                   y_scale=torch.zeros(5), stream=0)
+    with pytest.raises(ValueError, match="weight has 4 elements"):
+        rn.norm_scale_shift_fwd_ex(x, x, torch.zeros(4), None, row, row, 2, 3, 8, rn.RN_WEIGHT,
+                                   affine_dtype=rn.RN_DTYPE_F32, stream=0)
+    with pytest.raises(ValueError, match="is on meta but other operands are on cpu"):
+        rn.norm_scale_shift_fwd(x, x, None, None, row, torch.zeros(8, device="meta", **bf), 2, 3,
+                                8, 0, stream=0)
+    # int addresses are the C ABI's business: passed through unchecked
+    assert rn._check_tensors((("y", 1234, 10 ** 9),)) is None
+
+
 def test_inputs_may_share_memory(rn):
     # scale and shift (read-only) may be the same buffer; an empty problem has
     # no extents at all
