@@ -312,3 +312,52 @@ def test_ex_empty_problem_and_null_ext(rn):
     st = rn._lib.norm_scale_shift_fwd_ex(addr(0), addr(2), None, None, addr(7), addr(8), 0, 4,
                                          64, 0, rn._layout((0, 0)), 1e-6, None, None)
     assert st == 0, rn.last_error()
+
+
+C_CLIENT = r"""
+#include <stdio.h>
+#include <string.h>
+#include "resnorm.h"
+
+int main(void) {
+  rn_launch_info info;
+  rn_layout bc = {RN_BCAST, 0}, fr = {RN_FRAME, 49};
+  if (strstr(rn_version(), "gfx950") == NULL) return 1;
+  if (rn_describe_launch(1, 176400, 5120, RN_GATE, 1, fr, fr, &info) != RN_OK) return 2;
+  printf("%d %d %d %lld\n", info.waves_per_row, info.vec_per_lane, info.rows_per_block,
+         (long long)info.grid_blocks);
+  /* error paths fail on the host, before any device work */
+  if (resnorm_fused_fwd(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 1, 16, 5120,
+                        RN_GATE, bc, bc, 1e-6f, NULL) != RN_EINVAL) return 3;
+  printf("%s\n", rn_last_error());
+  if (norm_scale_shift_fwd((void*)16, (const void*)4096, NULL, NULL, (const void*)8192,
+                           (const void*)12288, 1, 16, 20000, 0, bc, 1e-6f, NULL) != RN_EUNSUPPORTED)
+    return 4;
+  rn_ext ext = {RN_DTYPE_BF16, RN_DTYPE_FP8_E4M3, NULL};
+  if (norm_scale_shift_fwd_ex((void*)16, (const void*)(1 << 20), NULL, NULL, (const void*)(2 << 20),
+                              (const void*)(3 << 20), 1, 16, 5120, 0, bc, 1e-6f, &ext, NULL)
+      != RN_EINVAL) return 5;
+  printf("%s\n", rn_last_error());
+  return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(rn, tmp_path):
+    """A C11 program (gcc, -Wall -Wextra -Werror) includes the header, links
+    the library and runs its host-only calls: version, the launch planner,
+    and three argument errors that must be reported without any device work."""
+    import subprocess
+    src = tmp_path / "client.c"
+    src.write_text(C_CLIENT)
+    exe = tmp_path / "client"
+    inc = os.path.join(ROOT, "include")
+    libdir = os.path.dirname(rn.LIB_PATH)
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-I", inc, str(src), "-o",
+                    str(exe), "-L", libdir, "-lrnorm", "-Wl,-rpath," + libdir], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
+    lines = out.stdout.splitlines()
+    assert lines[0] == "1 10 4 44100"
+    assert "NULL" in lines[1]
+    assert "y_scale" in lines[2]
