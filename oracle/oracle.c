@@ -190,7 +190,7 @@ static double operand(const void* p, int f32, int64_t c) {
  * Output by y_dtype: bf16 (y is uint16_t), binary32 (float, nearest-even
  * cast of t), or FP8 E4M3 with a per-row scale: y_scale = max|t| / 448 as a
  * binary32 value, and each element is the E4M3 rounding of t / y_scale
- * (0 when the row is all zeros).
+ * (when y_scale is 0: 0 for finite elements, NaN for NaN ones).
  */
 static void norm_row(const double* h, double* t, int64_t D, int is_rms, double eps,
                      const void* w, const void* bias, int affine_f32,
@@ -226,8 +226,11 @@ static void norm_row(const double* h, double* t, int64_t D, int is_rms, double e
       if (fabs(t[c]) > amax) amax = fabs(t[c]);
     float s = (float)(amax / 448.0);
     *y_scale = s;
+    /* A row whose elements are all zero or NaN has scale 0: its zeros encode
+     * as 0 and its NaNs stay NaN. */
     for (int64_t c = 0; c < D; ++c)
-      ((uint8_t*)y_row)[c] = s > 0.0f ? orc_f64_to_e4m3(t[c] / (double)s) : 0;
+      ((uint8_t*)y_row)[c] = s > 0.0f ? orc_f64_to_e4m3(t[c] / (double)s)
+                                      : (isnan(t[c]) ? orc_f64_to_e4m3(t[c]) : 0);
   }
 }
 

@@ -336,7 +336,9 @@ void row_kernel(const RowArgs a) {
       }
   }
   float var = row_reduce<W>(sq, Add{}, red_sq, wave, slot) * inv_d;
-  var = var > 0.f ? var : 0.f;
+  // Rounding can leave the variance slightly negative: lift it to 0.  A NaN
+  // variance (a row holding an infinity or a NaN) must stay NaN.
+  var = var < 0.f ? 0.f : var;
   const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
 
   // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v

@@ -545,7 +545,9 @@ def pin_fp8_rows(o, seed: int = 15):
     values.  Random rows: s is the binary32 rounding of max|t| / 448; the
     largest code decodes to +-448; every element decodes to t within half an
     E4M3 step (2^-4 relative, or s * 2^-10 for subnormals); an all-zero row gives
-    s = 0 and zero codes."""
+    s = 0 and zero codes; NaN elements stay out of the maximum and encode as
+    torch's cast of NaN, also in a row whose other elements are all zero
+    (s = 0)."""
     D = 16
     vals = np.array([448, -3.5, 0.25, 1.0625, 1.1875, -0.001953125, 0, 100, -448, 2 ** -7,
                      13, -17, 0.5, 7.5, 240, -0.75])
@@ -573,6 +575,24 @@ def pin_fp8_rows(o, seed: int = 15):
     y, _, s = o.nss(z, None, None, _zeros(1, D), _zeros(1, D), 1, 3, D, False, want_t=True,
                     y_dtype=2)
     assert np.all(s == 0) and np.all(y == 0)
+    # NaN elements: an RMSNorm row holding +Inf has rstd 0, so with scale = -1
+    # and shift = 0 it is t = 0 except NaN (Inf * 0) where the Inf was; a
+    # LayerNorm row holding NaN is NaN throughout.  Both rows get s = 0.
+    nan_code = _torch_e4m3(np.array([np.nan], np.float32))[0]
+    xr = synth.random_bf16((1, D), seed, 2)
+    xr[0, 3] = 0x7F80
+    y, t, s = o.nss(xr, None, None, _const(1, D, -1.0), _zeros(1, D), 1, 1, D, True, want_t=True,
+                    y_dtype=2)
+    assert s[0] == 0 and y[0, 3] == nan_code and np.all(np.delete(y[0], 3) == 0)
+    assert np.isnan(t[0, 3]) and np.all(np.delete(t[0], 3) == 0)
+    xn = synth.random_bf16((1, D), seed, 3)
+    xn[0, 9] = 0x7FC0
+    y, _, s = o.nss(xn, None, None, sc, shr, 1, 1, D, False, want_t=True, y_dtype=2)
+    assert s[0] == 0 and np.all(y[0] == nan_code)
+    # a NaN next to finite values: the scale comes from the finite ones
+    y, t, s = o.nss(xr, None, None, sc, shr, 1, 1, D, True, want_t=True, y_dtype=2)
+    fin = ~np.isnan(t[0])
+    assert s[0] == np.float32(np.abs(t[0][fin]).max() / 448.0) and y[0, 3] == nan_code
 
 
 FAST_PINS = [pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,

@@ -381,3 +381,56 @@ def test_tensors_over_4gib(rn, orc):
         check_y_f32(rows_of(y32, r0, n).cpu().numpy(), y_ref, "over 4 GiB f32, rows %d" % r0)
     del y32, ro, dev
     torch.cuda.empty_cache()
+
+
+def test_degenerate_rows_ext_outputs(rn, orc):
+    """Rows holding an infinity or a NaN, a residual sum that overflows to
+    Inf, an all-zero row and a constant row, with binary32 and FP8 E4M3 y:
+    NaN exactly where the oracle's is (NaN-ness, not payload or sign), equal
+    infinities, the per-row FP8 scales equal (NaN / Inf included), and every
+    finite element at its usual bar."""
+    D, L = 1024, 6
+    x = synth.random_bf16((L, D), 78, 1)
+    r = synth.random_bf16((L, D), 78, 2)
+    x[0, 5] = 0x7F80
+    x[1, 7] = 0x7FC0
+    x[2, :] = 0x7F7F
+    r[2, :] = 0x7F7F
+    x[3, :] = 0
+    r[3, :] = 0
+    x[4, :] = 0x3FC0
+    r[4, :] = 0
+    g = np.full((1, D), 0x3F80, np.uint16)
+    sc = synth.random_bf16((1, D), 78, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 78, 7, a=0.0, b=0.1)
+    d = {k: to_dev(v) for k, v in (("x", x), ("r", r), ("g", g), ("sc", sc), ("sh", sh))}
+    for rms in (False, True):
+        flags = (rn.RN_RMS if rms else 0) | rn.RN_GATE
+        ro = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+        y32 = torch.empty((L, D), dtype=torch.float32, device="cuda")
+        rn.resnorm_fused_fwd_ex(y32, ro, d["x"], d["r"], d["g"], None, None, d["sc"], d["sh"], 1, L,
+                                D, flags, (BCAST, 0), (BCAST, 0), 1e-6, y_dtype=rn.RN_DTYPE_F32)
+        y8 = torch.empty((L, D), dtype=torch.float8_e4m3fn, device="cuda")
+        ys = torch.empty((L,), dtype=torch.float32, device="cuda")
+        rn.resnorm_fused_fwd_ex(y8, ro, d["x"], d["r"], d["g"], None, None, d["sc"], d["sh"], 1, L,
+                                D, flags, (BCAST, 0), (BCAST, 0), 1e-6,
+                                y_dtype=rn.RN_DTYPE_FP8_E4M3, y_scale=ys)
+        torch.cuda.synchronize()
+        what = "rms=%s" % rms
+        ref32 = orc.fused(x, r, g, None, None, sc, sh, 1, L, D, rms, y_dtype=1)[0]
+        got32 = y32.cpu().numpy()
+        assert np.array_equal(np.isnan(got32), np.isnan(ref32)), what + " f32 NaN positions"
+        inf = np.isinf(ref32)
+        assert np.array_equal(got32[inf], ref32[inf]), what + " f32 infinities"
+        fin = np.isfinite(ref32)
+        check_y_f32(got32[fin], ref32[fin], what + " f32")
+        q_ref, _, _, s_ref = orc.fused(x, r, g, None, None, sc, sh, 1, L, D, rms, y_dtype=2)
+        q_got, s_got = y8.view(torch.uint8).cpu().numpy(), ys.cpu().numpy()
+        assert np.array_equal(np.isnan(s_got), np.isnan(s_ref)), what + " scale NaN"
+        assert np.array_equal(np.isinf(s_got), np.isinf(s_ref)), what + " scale Inf"
+        sf = np.isfinite(s_ref)
+        np.testing.assert_allclose(s_got[sf], s_ref[sf], rtol=2.0 ** -20, atol=0)
+        dg, dr = E4M3[q_got], E4M3[q_ref]
+        assert np.array_equal(np.isnan(dg), np.isnan(dr)), what + " FP8 NaN positions"
+        ok = np.isnan(dr) | (np.abs(dg - dr) <= e4m3_step(np.where(np.isnan(dr), 0, dr)) * (1 + 1e-12))
+        assert ok.all(), what + " FP8 codes more than one step away"

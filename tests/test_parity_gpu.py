@@ -441,3 +441,65 @@ def test_hip_graph_capture_and_replay(rn, orc):
         assert same > 0.999, same
         # eager work between replays
         torch.add(bufs["x"], 1.0).sum().item()
+
+
+def test_degenerate_rows(rn, orc):
+    """Rows with an Inf or NaN element, residual sums that overflow binary32 to
+    Inf, all-zero rows, rows of bf16 subnormals, constant rows and rows of
+    large magnitude (|x| ~ 2^50), through both ops and both norms:
+    residual_out bit-exact (NaN compared as NaN); y NaN exactly where the
+    oracle's is, equal infinities, and the usual bar on every finite element.
+    The row statistics are binary32 sums, so a row whose sum of squares
+    overflows binary32 (here: the norm-only op on the row of bf16-maximum x)
+    is outside the kernels' range and left out of the norm-only comparison."""
+    import torch
+    D, L = 1024, 8
+    x = synth.random_bf16((L, D), 77, 1)
+    r = synth.random_bf16((L, D), 77, 2)
+    x[0, 5] = 0x7F80                      # +Inf in x
+    x[1, 7] = 0x7FC0                      # NaN in x
+    r[2, 3] = 0xFF80                      # -Inf in the residual
+    x[3, :] = 0x7F7F                      # bf16 max: residual + x overflows to +Inf
+    r[3, :] = 0x7F7F
+    x[4, :] = 0
+    r[4, :] = 0
+    x[5, :] = np.arange(D, dtype=np.uint16) % 0x7F + 1   # positive bf16 subnormals
+    r[5, :] = 0
+    x[6, :] = 0x3FC0                      # 1.5 everywhere
+    r[6, :] = 0
+    x[7, :] = (x[7, :] & 0x807F) | 0x5880  # random signs and mantissas, magnitude 2^50
+    r[7, :] = 0
+    g = synth.random_bf16((1, D), 77, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
+    g[0, :] = 0x3F80                      # gate 1: rows keep their designed sums
+    sc = synth.random_bf16((1, D), 77, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 77, 7, a=0.0, b=0.1)
+    d = {k: to_dev(v) for k, v in (("x", x), ("r", r), ("g", g), ("sc", sc), ("sh", sh))}
+
+    def same(got, ref, what):
+        gnan = (got & 0x7FFF) > 0x7F80
+        rnan = (ref & 0x7FFF) > 0x7F80
+        assert np.array_equal(gnan, rnan), "%s: NaN positions differ at %s" % (
+            what, np.argwhere(gnan != rnan)[:4].tolist())
+        inf_r = (ref & 0x7FFF) == 0x7F80
+        assert np.array_equal(got[inf_r], ref[inf_r]), what + ": infinities differ"
+        fin = ~rnan & ~inf_r
+        compare_outputs(got[fin], ref[fin], what=what)
+
+    for rms in (False, True):
+        flags = (rn.RN_RMS if rms else 0) | rn.RN_GATE
+        y = torch.empty_like(d["x"])
+        ro = torch.empty_like(d["x"])
+        rn.resnorm_fused_fwd(y, ro, d["x"], d["r"], d["g"], None, None, d["sc"], d["sh"], 1, L, D,
+                             flags, (BCAST, 0), (BCAST, 0), 1e-6)
+        torch.cuda.synchronize()
+        y_ref, ro_ref, _ = orc.fused(x, r, g, None, None, sc, sh, 1, L, D, rms)
+        same(to_host(ro), ro_ref, "fused rms=%s residual_out" % rms)
+        same(to_host(y), y_ref, "fused rms=%s y" % rms)
+        assert (ro_ref[3] == 0x7F80).all()
+        yn = torch.empty_like(d["x"])
+        rn.norm_scale_shift_fwd(yn, d["x"], None, None, d["sc"], d["sh"], 1, L, D,
+                                rn.RN_RMS if rms else 0, (BCAST, 0), 1e-6)
+        torch.cuda.synchronize()
+        yn_ref, _ = orc.nss(x, None, None, sc, sh, 1, L, D, rms)
+        keep = np.arange(L) != 3              # sum of squares beyond binary32
+        same(to_host(yn)[keep], yn_ref[keep], "norm-only rms=%s y" % rms)
