@@ -167,7 +167,8 @@ const char* rn_last_error(void);
 /* Launch shape the library would use for a problem (host-only query; no
  * device work, usable without a GPU): 16-byte vectors per lane and operand,
  * waves per activation row, waves and rows per workgroup, workgroup size and
- * grid size.  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
+ * the number of workgroups (laid out over a second grid dimension when one
+ * dimension would exceed 2^32 - 1 work-items).  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
  * (0); the layouts matter because per-row modulation operands add HBM
  * streams, which changes the preferred shape, and so does the row count
  * (problems of at most 512 rows are latency-bound).  The answer is for bf16

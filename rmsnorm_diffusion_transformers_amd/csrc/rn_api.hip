@@ -286,8 +286,15 @@ rn_status run(const Problem& p, void* stream) {
 
   const rn::Shape shape = rn::kShapes[vi];
   const int64_t blocks = (R + shape.rpb - 1) / shape.rpb;
+  const int64_t threads = (int64_t)rn::kWaveSize * shape.w * shape.rpb;
+  // A dispatch counts work-items per grid dimension in 32 bits: beyond that
+  // the workgroups continue in y (the kernel numbers them x-fastest; the
+  // surplus of the last y row finds no row and exits).
+  const int64_t max_x = (int64_t)UINT32_MAX / threads;
+  const int64_t gx = blocks < max_x ? blocks : max_x;
+  const int64_t gy = (blocks + gx - 1) / gx;
   void* args[] = {&a};
-  hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)blocks), dim3(rn::kWaveSize * shape.w * shape.rpb), args, 0,
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((uint32_t)gx, (uint32_t)gy), dim3((uint32_t)threads), args, 0,
                                  (hipStream_t)stream);
   if (e != hipSuccess) return fail(RN_ELAUNCH, "hipLaunchKernel failed: %s", hipGetErrorString(e));
   return RN_OK;

@@ -216,7 +216,9 @@ void row_kernel(const RowArgs a) {
   const uint32_t lane = threadIdx.x & (kWaveSize - 1);
   const uint32_t slot = wave / W;  // row slot in the workgroup
   const uint32_t part = wave % W;  // which contiguous part of the row this wave holds
-  const uint32_t row = blockIdx.x * RPB + slot;
+  // Workgroups are numbered x-fastest over a 2D grid: the dispatch counts
+  // work-items per dimension in 32 bits, so large problems spill into y.
+  const uint32_t row = (blockIdx.y * gridDim.x + blockIdx.x) * RPB + slot;
   // With W > 1 every wave must reach the barriers, so a wave past the last
   // row keeps going with its memory operations disabled (zero-range buffers).
   const bool live = row < a.rows;

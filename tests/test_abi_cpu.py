@@ -97,6 +97,7 @@ def nss(rn, **kw):
     (dict(B=-1), 1, "negative"),
     (dict(L=-5), 1, "negative"),
     (dict(B=1 << 20, L=1 << 12), 2, "2^31"),
+    (dict(B=1, L=1 << 31), 2, "2^31"),
     (dict(eps=-1e-6), 1, "eps"),
     (dict(eps=float("nan")), 1, "eps"),
     (dict(eps=float("inf")), 1, "eps"),

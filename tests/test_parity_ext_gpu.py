@@ -434,3 +434,106 @@ def test_degenerate_rows_ext_outputs(rn, orc):
         assert np.array_equal(np.isnan(dg), np.isnan(dr)), what + " FP8 NaN positions"
         ok = np.isnan(dr) | (np.abs(dg - dr) <= e4m3_step(np.where(np.isnan(dr), 0, dr)) * (1 + 1e-12))
         assert ok.all(), what + " FP8 codes more than one step away"
+
+
+def test_maximum_row_count(rn, orc):
+    """B * L = 2^31 - 1 rows (the largest the ABI accepts) at D = 8: 34 GB per
+    tensor and a grid of 2^29 workgroups.  The inputs are a seeded block of
+    65536 rows tiled over the tensor on the device; sampled rows (the first,
+    around 2^30, the last) against the oracle, for the norm-only op and the
+    fused op (per-batch scale/shift, broadcast gate)."""
+    D, T = 8, 65536
+    L = (1 << 31) - 1
+    info = rn.describe_launch(1, L, D, 0, False)
+    assert info["grid_blocks"] == (L + info["rows_per_block"] - 1) // info["rows_per_block"]
+    tiles = {k: synth.random_bf16((T, D), 31, t) for k, t in (("x", 1), ("residual", 2))}
+    g = synth.random_bf16((1, D), 31, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
+    sc = synth.random_bf16((1, D), 31, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 31, 7, a=0.0, b=0.1)
+    dg, dsc, dsh = to_dev(g), to_dev(sc), to_dev(sh)
+
+    def tiled(k):
+        t = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+        tile = to_dev(tiles[k])
+        full = (L // T) * T
+        t[:full].view(-1, T, D).copy_(tile.unsqueeze(0).expand(L // T, T, D))
+        t[full:].copy_(tile[:L - full])
+        return t
+
+    samples = [0, (1 << 30) - 5, L - 20]
+
+    def host_rows(k, r0, n):
+        return tiles[k][np.arange(r0, r0 + n) % T]
+
+    log("maximum rows: norm-only, %d rows" % L)
+    x = tiled("x")
+    y = torch.empty_like(x)
+    rn.norm_scale_shift_fwd(y, x, None, None, dsc, dsh, 1, L, D, 0, (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    for r0 in samples:
+        n = min(20, L - r0)
+        xs = host_rows("x", r0, n)
+        y_ref, _ = orc.nss(xs, None, None, sc, sh, 1, L, D, False, row0=r0, nrows=n)
+        compare_outputs(to_host(y[r0:r0 + n]), y_ref, what="max rows nss at %d" % r0)
+    del y
+    log("maximum rows: fused")
+    r = tiled("residual")
+    y = torch.empty_like(x)
+    ro = torch.empty_like(x)
+    rn.resnorm_fused_fwd(y, ro, x, r, dg, None, None, dsc, dsh, 1, L, D, rn.RN_GATE, (BCAST, 0),
+                         (FRAME, 1), 1e-6)
+    torch.cuda.synchronize()
+    for r0 in samples:
+        n = min(20, L - r0)
+        y_ref, ro_ref, _ = orc.fused(host_rows("x", r0, n), host_rows("residual", r0, n), g, None,
+                                     None, sc, sh, 1, L, D, False, (BCAST, 0), (FRAME, 1), 1e-6,
+                                     row0=r0, nrows=n)
+        compare_outputs(to_host(y[r0:r0 + n]), y_ref, to_host(ro[r0:r0 + n]), ro_ref,
+                        "max rows fused at %d" % r0)
+    del x, r, y, ro
+    torch.cuda.empty_cache()
+
+
+def test_two_dimensional_grid_ten_waves(rn, orc):
+    """Ten waves per row (640-thread workgroups: per-row gate, D = 2560) over
+    6,711,887 rows, just past the 6,710,886 workgroups one grid dimension can
+    hold, so the launch spills into a second dimension: rows either side of
+    the seam and the last rows against the oracle (five 34 GB tensors)."""
+    D, T = 2560, 4096
+    L = 6711887
+    flags = rn.RN_GATE
+    info = rn.describe_launch(1, L, D, flags, True, (ROW, 0), (BCAST, 0))
+    assert info["waves_per_row"] == 10 and info["block_threads"] == 640
+    seam = (2 ** 32 - 1) // 640
+    assert info["grid_blocks"] > seam
+    tiles = {k: synth.random_bf16((T, D), 32, t) for k, t in (("x", 1), ("residual", 2))}
+    tiles["gate"] = synth.random_bf16((T, D), 32, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
+    sc = synth.random_bf16((1, D), 32, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 32, 7, a=0.0, b=0.1)
+
+    def tiled(k):
+        t = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+        tile = to_dev(tiles[k])
+        full = (L // T) * T
+        t[:full].view(-1, T, D).copy_(tile.unsqueeze(0).expand(L // T, T, D))
+        t[full:].copy_(tile[:L - full])
+        return t
+
+    log("two-dimensional grid: %d rows x %d, ten waves per row" % (L, D))
+    dev = {k: tiled(k) for k in ("x", "residual", "gate")}
+    y = torch.empty_like(dev["x"])
+    ro = torch.empty_like(dev["x"])
+    rn.resnorm_fused_fwd(y, ro, dev["x"], dev["residual"], dev["gate"], None, None, to_dev(sc),
+                         to_dev(sh), 1, L, D, flags, (ROW, 0), (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    for r0 in (0, seam - 3, L - 4):
+        n = min(8, L - r0)
+        rows = np.arange(r0, r0 + n) % T
+        # a per-row gate: the sampled rows as a problem of their own (rows are
+        # independent, and with broadcast scale/shift nothing else depends on r)
+        y_ref, ro_ref, _ = orc.fused(tiles["x"][rows], tiles["residual"][rows], tiles["gate"][rows],
+                                     None, None, sc, sh, 1, n, D, False, (ROW, 0), (BCAST, 0), 1e-6)
+        compare_outputs(to_host(y[r0:r0 + n]), y_ref, to_host(ro[r0:r0 + n]), ro_ref,
+                        "2D grid rows %d..%d" % (r0, r0 + n))
+    del dev, y, ro
+    torch.cuda.empty_cache()
