@@ -383,9 +383,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures this path on exactly one GPU (the row-wise op needs no "
-              "communication; see the sharding note in the design document); --gpus %d is "
-              "not supported" % args.gpus, file=sys.stderr)
+        print("bench.py measures this path on exactly one GPU; --gpus %d is not supported. "
+              "Rows are independent, so several GPUs would each run the one-GPU kernel on a "
+              "contiguous range of rows with no communication." % args.gpus, file=sys.stderr)
         sys.exit(2)
 
     import torch
