@@ -20,7 +20,7 @@
 //     the end of a ragged row read zeros and their stores are dropped by the
 //     hardware range check.
 //   * All loads of a row -- x, residual, gate, weight, bias, scale, shift --
-//     are issued before its first store.  Loads and stores share the in-order
+//     are issued before its first store (in a measured order).  Loads and stores share the in-order
 //     vmcnt counter on gfx9, so a load issued after a store could only be
 //     waited for together with that store; issuing every load first keeps the
 //     store latency off the critical path.
@@ -48,6 +48,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "rn_args.h"
 
@@ -112,6 +114,42 @@ struct Add {
 struct Max {
   __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
 };
+// Maximum that propagates NaN (either operand NaN -> NaN), the same on both
+// partners of a reduction step.
+struct MaxNaN {
+  __device__ __forceinline__ float operator()(float a, float b) const {
+    return (a > b || a != a) ? a : b;
+  }
+};
+
+// Whether a binary32 row statistic overflowed, decided the same way by every
+// wave of the workgroup (a branch on it holds barriers when rows span
+// several waves): from the row's own total when the workgroup holds one row
+// or each wave is a row of its own; otherwise from the partial sums every
+// row of the workgroup left in LDS.
+template <int W, int RPB>
+__device__ __forceinline__ bool overflowed(float total, const float* red) {
+  bool any;
+  if constexpr (W == 1 || RPB == 1) {
+    any = !__builtin_isfinite(total);
+  } else {
+    any = false;
+#pragma unroll
+    for (int q = 0; q < RPB; ++q) {
+      float t = red[q * W];
+#pragma unroll
+      for (int p = 1; p < W; ++p) t += red[q * W + p];
+      any = any || !__builtin_isfinite(t);
+    }
+  }
+  return __builtin_amdgcn_readfirstlane((int)any) != 0;
+}
+
+// Power of two s = 2^-k that brings a finite, nonzero magnitude m into
+// [1, 2); k = 0 (s = 1) when m is 0, infinite or NaN.
+__device__ __forceinline__ int scale_exp(float m) {
+  return (__builtin_isfinite(m) && m > 0.f) ? __builtin_amdgcn_frexp_expf(m) - 1 : 0;
+}
 
 // Reduction over the 64 lanes of a wave; every lane returns the same bits.
 // Each step combines a lane's value with its partner's in an order that is
@@ -239,41 +277,71 @@ void row_kernel(const RowArgs a) {
   const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * (a.d * 2u), row_bytes);
 
   // ---- every load of the row, before any store ----
+  // The order of the groups of loads is fixed at compile time (a run-time
+  // choice merges paths whose loads are counted in different orders, and
+  // the waits after the merge then cover every load).  Measured on MI355X
+  // at L = 90000-176400 (1-5 % on the whole kernel): ten waves per row (the
+  // shapes chosen when per-row scale/shift or gate are streamed from HBM):
+  // the activation rows, gate, weight/bias, scale/shift; otherwise the
+  // shared rows ahead of the activation rows -- without affine: gate,
+  // scale/shift, activation rows; with affine: scale/shift, activation
+  // rows, gate, weight/bias.
   u32x4 h[VPT];  // x (norm-only) or residual, later the bf16-packed residual_out
   [[maybe_unused]] u32x4 xv[VPT];
   [[maybe_unused]] u32x4 gv[VPT];
   [[maybe_unused]] AffineRow<OP::aff32, VPT> wv, bv;
   u32x4 sc[VPT], sh[VPT];
-  if constexpr (OP::fused) {
-    const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_r, base + v * 1024u);
-    if constexpr (OP::gate) {
+  const uint32_t aff_bytes = live ? a.d * (OP::aff32 ? 4u : 2u) : 0u;
+  auto load_gate = [&]() {
+    if constexpr (OP::fused && OP::gate) {
       const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, r, b, l);
       const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * (a.d * 2u), row_bytes);
 #pragma unroll
       for (int v = 0; v < VPT; ++v) gv[v] = load16<kPolicyDefault, PL>(rs_g, base + v * 1024u);
     }
-  } else {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
-  }
-  const uint32_t aff_bytes = live ? a.d * (OP::aff32 ? 4u : 2u) : 0u;
-  if constexpr (OP::has_w) wv.template load<PL>(row_rsrc(a.weight, aff_bytes), base);
-  if constexpr (OP::has_b) bv.template load<PL>(row_rsrc(a.bias, aff_bytes), base);
+  };
   // per-row scale/shift stream like the activations; shared rows stay cached
-  if (a.ss_kind == 1) {
+  auto load_ss = [&](auto policy) {
+    constexpr int P = decltype(policy)::value;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) sc[v] = load16<kPolicyStream, PL>(rs_sc, base + v * 1024u);
+    for (int v = 0; v < VPT; ++v) sc[v] = load16<P, PL>(rs_sc, base + v * 1024u);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) sh[v] = load16<kPolicyStream, PL>(rs_sh, base + v * 1024u);
+    for (int v = 0; v < VPT; ++v) sh[v] = load16<P, PL>(rs_sh, base + v * 1024u);
+  };
+  auto load_affine = [&]() {
+    if constexpr (OP::has_w) wv.template load<PL>(row_rsrc(a.weight, aff_bytes), base);
+    if constexpr (OP::has_b) bv.template load<PL>(row_rsrc(a.bias, aff_bytes), base);
+  };
+  auto load_rows = [&]() {
+    if constexpr (OP::fused) {
+      const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_r, base + v * 1024u);
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
+    }
+  };
+  auto load_ss_any = [&]() {
+    if (a.ss_kind == 1) load_ss(std::integral_constant<int, kPolicyStream>{});
+    else load_ss(std::integral_constant<int, kPolicyDefault>{});
+  };
+  if constexpr (W == 10) {
+    load_rows();
+    load_gate();
+    load_affine();
+    load_ss_any();
+  } else if constexpr (OP::has_w) {
+    load_ss_any();
+    load_rows();
+    load_gate();
+    load_affine();
   } else {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) sc[v] = load16<kPolicyDefault, PL>(rs_sc, base + v * 1024u);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) sh[v] = load16<kPolicyDefault, PL>(rs_sh, base + v * 1024u);
+    load_gate();
+    load_ss_any();
+    load_rows();
   }
 
   // ---- residual update (fused) ----
@@ -312,6 +380,32 @@ void row_kernel(const RowArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
     mean = row_reduce<W>(sum, Add{}, red_sum, wave, slot) / (float)a.d;
+    // Finite values summing beyond the binary32 range (|h| ~ 1e34 and more):
+    // the mean again from h * 2^-k, k from the row's largest magnitude (a
+    // power of two, exact for every element that stays inside the binary32
+    // range; the others are negligible next to the largest), scaled back.
+    // Done before the variance pass, so that pass and the epilogue share
+    // the centred values.  A row holding an infinity or a NaN keeps its
+    // non-finite mean.
+    if (overflowed<W, RPB>(mean, red_sum)) {
+      float m = 0.f;
+      const MaxNaN mx;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          m = mx(m, mx(__builtin_fabsf(lo_f32(h[v][j])), __builtin_fabsf(hi_f32(h[v][j]))));
+      m = row_reduce<W>(m, mx, red_max, wave, slot);
+      const int k = __builtin_isfinite(mean) ? 0 : scale_exp(m);
+      const float s = __builtin_ldexpf(1.0f, -k);
+      float sum2 = 0.f;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum2 += lo_f32(h[v][j]) * s + hi_f32(h[v][j]) * s;
+      const float mean2 = row_reduce<W>(sum2, Add{}, red_sum, wave, slot) / (float)a.d;
+      if (k != 0) mean = __builtin_ldexpf(mean2, k);
+    }
 #pragma unroll
     for (int v = 0; v < VPT; ++v) {
       float part_sq = 0.f;
@@ -341,7 +435,44 @@ void row_kernel(const RowArgs a) {
   // Rounding can leave the variance slightly negative: lift it to 0.  A NaN
   // variance (a row holding an infinity or a NaN) must stay NaN.
   var = var < 0.f ? 0.f : var;
-  const float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+  float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+  // Finite centred values whose squares sum beyond the binary32 range
+  // (|h - mean| ~ 1e17-1e19 and more): the variance again from
+  // (h - mean) * 2^-k, k from the largest centred magnitude, and
+  // rstd = 2^-k / sqrt(var' + eps * 2^-2k).  Only rstd changes, so the
+  // epilogue is the same for every row.
+  if (overflowed<W, RPB>(var, red_sq)) {
+    float m = 0.f;
+    const MaxNaN mx;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in_row = base / 16u + (uint32_t)(v * kWaveSize) < a.nvec;
+        const float d0 = in_row ? __builtin_fabsf(lo_f32(h[v][j]) - mean) : 0.f;
+        const float d1 = in_row ? __builtin_fabsf(hi_f32(h[v][j]) - mean) : 0.f;
+        m = mx(m, mx(d0, d1));
+      }
+    m = row_reduce<W>(m, mx, red_max, wave, slot);
+    const int k = __builtin_isfinite(var) ? 0 : scale_exp(m);
+    const float s = __builtin_ldexpf(1.0f, -k);
+    float sq2 = 0.f;
+#pragma unroll
+    for (int v = 0; v < VPT; ++v) {
+      float part_sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float d0 = (lo_f32(h[v][j]) - mean) * s;
+        const float d1 = (hi_f32(h[v][j]) - mean) * s;
+        part_sq = __builtin_fmaf(d0, d0, part_sq);
+        part_sq = __builtin_fmaf(d1, d1, part_sq);
+      }
+      sq2 += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
+    }
+    float var2 = row_reduce<W>(sq2, Add{}, red_sq, wave, slot) * inv_d;
+    var2 = var2 < 0.f ? 0.f : var2;
+    if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
+  }
 
   // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v
   auto tval = [&](int v, int j, int k) -> float {

@@ -9,7 +9,10 @@ assembly hipcc writes for them:
     in the FP8 kernels only);
   * no scratch (private segment 0, no VGPR spills) and no LDS for one wave
     per row;
-  * the wave reductions are DPP adds plus permlane16/permlane32 swaps;
+  * the wave reductions are DPP steps plus permlane16/permlane32 swaps: the
+    mean and the variance on the common path, and on the paths for rows
+    whose binary32 sums overflow, a NaN-propagating maximum and a rescaled
+    sum each for the mean and for the variance;
   * the instruction counts per row match the design: 10 vectors per lane of
     each of x, residual, gate, and scale/shift (twice: the per-row and the
     shared-row paths), 20 stores, 80 bf16 packs.
@@ -68,16 +71,19 @@ def test_headline_kernel_memory_traffic_is_128bit(fused_asm):
     body, meta = _kernel(fused_asm, HEADLINE)
     assert not re.search(r"^\s+(global|flat|scratch)_", body, re.M)
     assert not re.search(r"^\s+buffer_(load|store)_(dword|dwordx2|dwordx3|short|byte|ubyte|ushort|sbyte|sshort)\b", body, re.M)
-    assert _count(body, "buffer_load_dwordx4") == 70     # x, r, gate 10 each; scale/shift 20 on each path
+    # x, residual, gate 10 vectors each; scale/shift 20 on each of the
+    # per-row and shared-row paths
+    assert _count(body, "buffer_load_dwordx4") == 70
     assert _count(body, "buffer_store_dwordx4") == 20    # residual_out, y
     assert _count(body, "v_cvt_pk_bf16_f32") == 80
 
 
 def test_headline_kernel_reductions_and_resources(fused_asm):
     body, meta = _kernel(fused_asm, HEADLINE)
-    assert _count(body, "v_add_f32_dpp") == 8            # two reductions x four DPP steps
-    assert _count(body, "v_permlane16_swap_b32_e32") == 2
-    assert _count(body, "v_permlane32_swap_b32_e32") == 2
+    assert _count(body, "v_add_f32_dpp") == 16           # (2 common + 2 overflow) sums x 4 steps
+    assert _count(body, "v_mov_b32_dpp") == 8            # 2 overflow-path maxima x 4 steps
+    assert _count(body, "v_permlane16_swap_b32_e32") == 6
+    assert _count(body, "v_permlane32_swap_b32_e32") == 6
     assert _count(body, "s_barrier") == 0                # one wave per row: no barrier
     assert not re.search(r"^\s+ds_", body, re.M)         # no LDS
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
@@ -94,9 +100,9 @@ def test_fp8_kernel_stores(tmp_path):
     body, meta = _kernel(asm, sym)
     assert _count(body, "buffer_store_dwordx2") == 10    # 8 FP8 bytes per lane per vector
     assert _count(body, "v_cvt_pk_fp8_f32") == 40
-    assert _count(body, "v_mov_b32_dpp") == 4            # the row maximum's DPP steps
-    assert _count(body, "v_add_f32_dpp") == 8            # mean and centred variance
-    assert _count(body, "v_permlane32_swap_b32_e32") == 3
+    assert _count(body, "v_mov_b32_dpp") == 12           # |t| maximum + 2 overflow-path maxima
+    assert _count(body, "v_add_f32_dpp") == 16           # mean and variance, + their overflow paths
+    assert _count(body, "v_permlane32_swap_b32_e32") == 7
     assert _count(body, "global_store_dword") == 1       # the per-row scale
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
     assert not re.search(r"^\s+(flat|scratch)_", body, re.M)

@@ -446,14 +446,13 @@ def test_hip_graph_capture_and_replay(rn, orc):
 def test_degenerate_rows(rn, orc):
     """Rows with an Inf or NaN element, residual sums that overflow binary32 to
     Inf, all-zero rows, rows of bf16 subnormals, constant rows and rows of
-    large magnitude (|x| ~ 2^50), through both ops and both norms:
-    residual_out bit-exact (NaN compared as NaN); y NaN exactly where the
-    oracle's is, equal infinities, and the usual bar on every finite element.
-    The row statistics are binary32 sums, so a row whose sum of squares
-    overflows binary32 (here: the norm-only op on the row of bf16-maximum x)
-    is outside the kernels' range and left out of the norm-only comparison."""
+    large magnitude (2^50; 2^100 and 2^126 with random signs, whose binary32
+    sums overflow and take the rescaled path; the bf16 maximum, constant),
+    through both ops and both norms: residual_out bit-exact (NaN compared as
+    NaN); y NaN exactly where the oracle's is, equal infinities, and the
+    usual bar on every finite element."""
     import torch
-    D, L = 1024, 8
+    D, L = 1024, 10
     x = synth.random_bf16((L, D), 77, 1)
     r = synth.random_bf16((L, D), 77, 2)
     x[0, 5] = 0x7F80                      # +Inf in x
@@ -469,6 +468,10 @@ def test_degenerate_rows(rn, orc):
     r[6, :] = 0
     x[7, :] = (x[7, :] & 0x807F) | 0x5880  # random signs and mantissas, magnitude 2^50
     r[7, :] = 0
+    x[8, :] = (x[8, :] & 0x807F) | 0x7180  # magnitude 2^100: squares overflow binary32
+    r[8, :] = 0
+    x[9, :] = (x[9, :] & 0x807F) | 0x7E80  # magnitude 2^126: sums overflow too
+    r[9, :] = 0
     g = synth.random_bf16((1, D), 77, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
     g[0, :] = 0x3F80                      # gate 1: rows keep their designed sums
     sc = synth.random_bf16((1, D), 77, 6, a=0.0, b=0.1)
@@ -501,5 +504,54 @@ def test_degenerate_rows(rn, orc):
                                 rn.RN_RMS if rms else 0, (BCAST, 0), 1e-6)
         torch.cuda.synchronize()
         yn_ref, _ = orc.nss(x, None, None, sc, sh, 1, L, D, rms)
-        keep = np.arange(L) != 3              # sum of squares beyond binary32
-        same(to_host(yn)[keep], yn_ref[keep], "norm-only rms=%s y" % rms)
+        same(to_host(yn), yn_ref, "norm-only rms=%s y" % rms)
+        assert not np.isnan(bf16_to_f64(yn_ref[[3, 8, 9]])).any()
+
+
+def test_rescaled_statistics_every_wave_count(rn, orc):
+    """Rows of magnitude 2^100 and 2^126 (random signs and mantissas), whose
+    binary32 sums overflow, interleaved with ordinary rows, for one, two
+    (two rows per workgroup: an overflowing row next to an ordinary one),
+    four and ten waves per row, both norms, fused and norm-only: every row
+    against the oracle."""
+    import torch
+    cases = [(5120, 2048, False, None), (3072, 300, False, None), (4096, 200, False, None),
+             (2560, 64, True, (ROW, 0))]
+    for D, L, fused, gl in cases:
+        x = synth.random_bf16((L, D), 90 + D, 1)
+        r = synth.random_bf16((L, D), 90 + D, 2)
+        rows = np.arange(L)
+        big = rows % 3 == 1
+        huge = rows % 7 == 3
+        x[big] = (x[big] & 0x807F) | 0x7180
+        x[huge] = (x[huge] & 0x807F) | 0x7E80
+        r[big | huge] = 0
+        g = synth.random_bf16((L if gl else 1, D), 90 + D, 3, dist=synth.UNIFORM, a=0.0, b=1.0)
+        if gl:
+            g[big | huge] = 0x3F80                # gate 1: residual_out = x on those rows
+        sc = synth.random_bf16((1, D), 90 + D, 6, a=0.0, b=0.1)
+        sh = synth.random_bf16((1, D), 90 + D, 7, a=0.0, b=0.1)
+        d = {k: to_dev(v) for k, v in (("x", x), ("r", r), ("g", g), ("sc", sc), ("sh", sh))}
+        for rms in (False, True):
+            flags = rn.RN_RMS if rms else 0
+            if fused:
+                flags |= rn.RN_GATE
+            info = rn.describe_launch(1, L, D, flags, fused, gl or (BCAST, 0), (BCAST, 0))
+            what = "D=%d L=%d fused=%s rms=%s W=%d RPB=%d" % (D, L, fused, rms, info["waves_per_row"],
+                                                             info["rows_per_block"])
+            log("rescaled statistics: " + what)
+            y = torch.empty_like(d["x"])
+            if fused:
+                ro = torch.empty_like(d["x"])
+                rn.resnorm_fused_fwd(y, ro, d["x"], d["r"], d["g"], None, None, d["sc"], d["sh"], 1,
+                                     L, D, flags, gl, (BCAST, 0), 1e-6)
+                torch.cuda.synchronize()
+                y_ref, ro_ref, _ = orc.fused(x, r, g, None, None, sc, sh, 1, L, D, rms, gl,
+                                             (BCAST, 0), 1e-6)
+                compare_outputs(to_host(y), y_ref, to_host(ro), ro_ref, what)
+            else:
+                rn.norm_scale_shift_fwd(y, d["x"], None, None, d["sc"], d["sh"], 1, L, D, flags,
+                                        (BCAST, 0), 1e-6)
+                torch.cuda.synchronize()
+                y_ref, _ = orc.nss(x, None, None, sc, sh, 1, L, D, rms)
+                compare_outputs(to_host(y), y_ref, what=what)
