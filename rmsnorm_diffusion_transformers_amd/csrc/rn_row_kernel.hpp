@@ -328,6 +328,12 @@ void row_kernel(const RowArgs a) {
     if (a.ss_kind == 1) load_ss(std::integral_constant<int, kPolicyStream>{});
     else load_ss(std::integral_constant<int, kPolicyDefault>{});
   };
+  // With one wave per row, a wave issues its loads at raised priority, so
+  // that the SIMD's other wave (busy with arithmetic or stores) does not
+  // delay them: measured ~1 % on the norm-only op, neutral on the fused one.
+  // Not with several waves per row: there it delays the row's other waves
+  // at the barriers (-12 % measured with binary32 weight/bias).
+  if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
   if constexpr (W == 10) {
     load_rows();
     load_gate();
@@ -343,6 +349,7 @@ void row_kernel(const RowArgs a) {
     load_ss_any();
     load_rows();
   }
+  if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
 
   // ---- residual update (fused) ----
   if constexpr (OP::fused) {
