@@ -20,7 +20,8 @@
 //     the end of a ragged row read zeros and their stores are dropped by the
 //     hardware range check.
 //   * All loads of a row -- x, residual, gate, weight, bias, scale, shift --
-//     are issued before its first store (in a measured order).  Loads and stores share the in-order
+//     are issued before its first store, in a measured order and (one wave
+//     per row) at raised wave priority.  Loads and stores share the in-order
 //     vmcnt counter on gfx9, so a load issued after a store could only be
 //     waited for together with that store; issuing every load first keeps the
 //     store latency off the critical path.
@@ -37,7 +38,9 @@
 //     reductions are DPP (xor 1, xor 2, half-row mirror, row mirror) then the
 //     gfx950 permlane16/permlane32 swaps; with W > 1 the per-wave totals are
 //     combined through LDS in a fixed order.  Every lane and every wave of a
-//     row ends with the bit-identical total.
+//     row ends with the bit-identical total.  Rows of finite values whose
+//     binary32 sums overflow are recomputed on the row scaled by a power of
+//     two (a branch the common path only tests for).
 //   * fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even; fp32
 //     denormals are kept in these kernels).
 //   * Output y is bf16, binary32, or OCP FP8 E4M3 with a per-row scale
@@ -314,11 +317,15 @@ void row_kernel(const RowArgs a) {
   };
   auto load_rows = [&]() {
     if constexpr (OP::fused) {
+      // the fused op's 2 x VPT streamed loads, spaced (one wave per row):
+      // measured 1 % faster at L = 176400, D = 5120; the norm-only op's VPT
+      // loads run best unspaced
+      constexpr int PLR = W == 1 ? kPaceFusedRowLoads : PL;
       const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
+      for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PLR>(rs_x, base + v * 1024u);
 #pragma unroll
-      for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_r, base + v * 1024u);
+      for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PLR>(rs_r, base + v * 1024u);
     } else {
 #pragma unroll
       for (int v = 0; v < VPT; ++v) h[v] = load16<kPolicyStream, PL>(rs_x, base + v * 1024u);
