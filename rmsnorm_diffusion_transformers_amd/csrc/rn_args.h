@@ -56,8 +56,9 @@ constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough
 // to saturate HBM with this access pattern.
 constexpr int kVgprBudget = 52;
-// Spacing of loads / stores, in units of 8 cycles (s_nop 7); the fused op's
-// x / residual loads with one wave per row have their own.
+// Spacing of loads / stores, in units of 8 cycles (s_nop 7); the streamed
+// row loads of the fused op with one wave per row, and of the norm-only op
+// with binary32 weight/bias, have their own.
 constexpr int kPaceLoads = 0;
 constexpr int kPaceFusedRowLoads = 1;
 constexpr int kPaceStores = 2;
