@@ -124,11 +124,12 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
 // Waves per row the planner aims for (0: the first compiled shape with W < 10
 // that fits the register budget); the measurements behind each rule are
 // listed with the shape table.
-int preferred_waves(int64_t R, int64_t D, int streams) {
+int preferred_waves(int64_t R, int64_t D, int streams, bool fused, bool one_wave_fits) {
   if (D >= rn::kManyStreamsMinD && streams >= 5) return 10;
   if (D < rn::kSplitMinD) return 0;
   if (R <= rn::kTinyRows && D > 4096 && D <= 5120) return 10;
   if (R <= rn::kSmallRows) return 4;
+  if (fused && one_wave_fits && R > 2 * rn::kSmallRows && R <= rn::kFusedOneWaveRows) return 0;
   if (R <= rn::kMidRowsSplit4 && (D >= rn::kManyStreamsMinD || R <= 2 * rn::kSmallRows))
     return D <= 3072 ? 2 : 4;
   if (R <= rn::kMidRows && D >= rn::kManyStreamsMinD) return 2;
@@ -138,8 +139,12 @@ int preferred_waves(int64_t R, int64_t D, int streams) {
 int shape_for(int64_t R, int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
-  const int want = preferred_waves(R, D, streams);
   auto covers = [&](const rn::Shape& s) { return (int64_t)rn::kWaveSize * s.w * s.vpt >= nvec; };
+  bool one_wave_fits = false;
+  for (int i = 0; i < rn::kNumShapes; ++i)
+    one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && covers(rn::kShapes[i]) &&
+                                      rn::kShapes[i].vpt * ops <= rn::kVgprBudget);
+  const int want = preferred_waves(R, D, streams, fused, one_wave_fits);
   if (want != 0) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];

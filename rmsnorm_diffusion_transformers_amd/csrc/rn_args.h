@@ -33,7 +33,11 @@ constexpr int kWaveSize = 64;
 //     the sweep at 64-4096 rows found these 10-30 % faster than one wave per
 //     row (e.g. 512 rows, D = 5120: 6.3 -> 5.3 us);
 //   * at most kTinyRows rows with 4096 < D <= 5120 use 10 waves of one
-//     vector each (L = 16, D = 5120: 2.8 us per call in a HIP graph).
+//     vector each (L = 16, D = 5120: 2.8 us per call in a HIP graph);
+//   * the fused op keeps one wave per row (when it fits the register budget)
+//     from 2 * kSmallRows + 1 up to kFusedOneWaveRows rows: with its loads
+//     ordered, spaced and prioritised it measured 5-18 % faster there than
+//     2 or 4 waves per row (e.g. D = 5120, 1024 rows: 9.8 -> 8.3 us).
 struct Shape {
   int w;
   int vpt;
@@ -51,6 +55,7 @@ constexpr int kTinyRows = 128;
 constexpr int kSmallRows = 256;
 constexpr int kMidRowsSplit4 = 768;
 constexpr int kMidRows = 1536;
+constexpr int kFusedOneWaveRows = 1024;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough

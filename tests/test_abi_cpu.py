@@ -201,6 +201,12 @@ def test_describe_launch(rn):
     assert plan(1536, 2048) == (1, 4) and plan(1000, 2040) == (1, 4)
     assert plan(100, 2040) == (1, 4)
     assert plan(16, 2552) == (4, 2)
+    # the fused op keeps one wave per row from 513 to 1024 rows where it fits
+    fplan = lambda R, D: tuple(rn.describe_launch(1, R, D, rn.RN_GATE, True)[k]  # noqa: E731
+                               for k in ("waves_per_row", "vec_per_lane"))
+    assert fplan(512, 5120) == (4, 3) and fplan(513, 5120) == (1, 10)
+    assert fplan(1024, 5120) == (1, 10) and fplan(1025, 5120) == (2, 5)
+    assert fplan(768, 6144) == (4, 3)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
     for D in range(8, 16385, 8):
         for fused, flags, gl, sl in ((False, 0, (0, 0), (0, 0)), (True, 14, (1, 0), (1, 0))):
