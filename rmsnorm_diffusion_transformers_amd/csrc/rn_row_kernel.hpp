@@ -247,7 +247,7 @@ void row_kernel(const RowArgs a) {
   constexpr int VPT = kShapes[SHAPE].vpt;
   constexpr int RPB = kShapes[SHAPE].rpb;
   constexpr int PL = kPaceLoads;
-  constexpr int PS = kPaceStores;
+  constexpr int PS = OP::out == kOutF32 ? kPaceStoresF32 : kPaceStores;
   static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
   [[maybe_unused]] __shared__ float red_sum[W * RPB];
   [[maybe_unused]] __shared__ float red_sq[W * RPB];
