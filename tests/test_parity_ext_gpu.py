@@ -105,6 +105,13 @@ def _run(rn, orc, seed, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtyp
     """One problem through the _ex entry point and the oracle; checks and
     returns a short statistic."""
     inp = _problem(seed, fused, gate_layout, aff, ss_layout, B, L, D)
+    return _run_inputs(rn, orc, inp, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype,
+                       eps, seed)
+
+
+def _run_inputs(rn, orc, inp, fused, rms, gate_layout, aff, ss_layout, B, L, D, y_dtype,
+                eps=1e-6, seed=-1):
+    """_run on given inputs (a dict as _problem returns)."""
     aff32 = aff in (3, 4)
     d = {}
     for k, v in inp.items():
@@ -537,3 +544,30 @@ def test_two_dimensional_grid_ten_waves(rn, orc):
                         "2D grid rows %d..%d" % (r0, r0 + n))
     del dev, y, ro
     torch.cuda.empty_cache()
+
+
+def test_rescaled_statistics_ext_outputs(rn, orc):
+    """Rows whose binary32 sums overflow (magnitudes 2^100 and 2^126), mixed
+    with ordinary rows, with binary32 and FP8 outputs and binary32
+    weight/bias, on shapes with one, two, four and ten waves per row: the
+    rescaled statistics and, for FP8, the row maximum that follows them in
+    the same workgroup."""
+    cases = [(5120, 2048, False, None, 0), (3072, 300, False, None, 0), (4096, 200, False, None, 0),
+             (2560, 64, True, (ROW, 0), 0), (5120, 600, True, (BCAST, 0), 4)]
+    for k, (D, L, fused, gl, aff) in enumerate(cases):
+        for y_dtype in (1, 2):
+            inp = _problem(1500 + k, fused, gl, aff, (BCAST, 0), 1, L, D)
+            rows = np.arange(L)
+            big, huge = rows % 3 == 1, rows % 7 == 3
+            inp["x"][big] = (inp["x"][big] & 0x807F) | 0x7180
+            inp["x"][huge] = (inp["x"][huge] & 0x807F) | 0x7E80
+            if fused:
+                inp["residual"][big | huge] = 0
+                if gl is not None and gl[0] == ROW:
+                    inp["gate"][big | huge] = 0x3F80
+            flags = (rn.RN_GATE if gl is not None else 0) | \
+                (rn.RN_WEIGHT | rn.RN_BIAS if aff else 0)
+            info = rn.describe_launch(1, L, D, flags, fused, gl or (BCAST, 0), (BCAST, 0))
+            log("rescaled statistics ext: D=%d L=%d fused=%s aff=%d y=%d W=%d" % (
+                D, L, fused, aff, y_dtype, info["waves_per_row"]))
+            _run_inputs(rn, orc, inp, fused, False, gl, aff, (BCAST, 0), 1, L, D, y_dtype)
