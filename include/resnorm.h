@@ -171,9 +171,10 @@ const char* rn_last_error(void);
  * dimension would exceed 2^32 - 1 work-items).  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
  * (0); the layouts matter because per-row modulation operands add HBM
  * streams, which changes the preferred shape, and so does the row count
- * (problems of at most 512 rows are latency-bound).  The answer is for bf16
- * weight/bias; binary32 weight/bias (the _ex entry points) hold twice the
- * registers per vector and may get a shorter per-wave span. */
+ * (small problems are latency-bound).  The answer is for bf16 weight/bias;
+ * rn_describe_launch_ex takes the element types of the *_ex entry points
+ * (binary32 weight/bias hold twice the registers per vector and may get a
+ * shorter per-wave span; the output type does not change the shape). */
 typedef struct {
   int32_t vec_per_lane;
   int32_t waves_per_row;
@@ -185,6 +186,11 @@ typedef struct {
 
 rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
                              rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info);
+/* The same for the *_ex entry points' element types (ext may be NULL: all
+ * bf16).  RN_EINVAL for an unknown affine_dtype. */
+rn_status rn_describe_launch_ex(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
+                                rn_layout gate_layout, rn_layout ss_layout, const rn_ext* ext,
+                                rn_launch_info* info);
 
 /* Library version string. */
 const char* rn_version(void);

@@ -81,6 +81,9 @@ def _load() -> ctypes.CDLL:
     lib.rn_describe_launch.argtypes = [I64, I64, I64, U32, ctypes.c_int32, rn_layout, rn_layout,
                                        ctypes.POINTER(rn_launch_info)]
     lib.rn_describe_launch.restype = ctypes.c_int
+    lib.rn_describe_launch_ex.argtypes = [I64, I64, I64, U32, ctypes.c_int32, rn_layout, rn_layout,
+                                          ctypes.POINTER(rn_ext), ctypes.POINTER(rn_launch_info)]
+    lib.rn_describe_launch_ex.restype = ctypes.c_int
     lib.rn_version.argtypes = []
     lib.rn_version.restype = ctypes.c_char_p
     return lib
@@ -254,11 +257,14 @@ def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
 
 
 def describe_launch(B, L, D, flags, fused=True, gate_layout=(RN_BCAST, 0),
-                    ss_layout=(RN_BCAST, 0)) -> dict:
-    """Launch shape the library picks for a problem (host-only query)."""
+                    ss_layout=(RN_BCAST, 0), affine_dtype=RN_DTYPE_BF16) -> dict:
+    """Launch shape the library picks for a problem (host-only query;
+    rn_describe_launch_ex)."""
     info = rn_launch_info()
-    _check(_lib.rn_describe_launch(int(B), int(L), int(D), int(flags), int(bool(fused)),
-                                   _layout(gate_layout), _layout(ss_layout), ctypes.byref(info)))
+    ext = rn_ext(int(affine_dtype), RN_DTYPE_BF16, None)
+    _check(_lib.rn_describe_launch_ex(int(B), int(L), int(D), int(flags), int(bool(fused)),
+                                      _layout(gate_layout), _layout(ss_layout), ctypes.byref(ext),
+                                      ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in rn_launch_info._fields_}
 
 

@@ -382,13 +382,17 @@ rn_status norm_scale_shift_fwd(void* y, const void* x, const void* weight, const
 
 const char* rn_last_error(void) { return g_err; }
 
-rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
-                             rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info) {
+rn_status rn_describe_launch_ex(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
+                                rn_layout gate_layout, rn_layout ss_layout, const rn_ext* ext,
+                                rn_launch_info* info) {
   g_err[0] = '\0';
   if (!info) return fail(RN_EINVAL, "info is NULL");
   rn_status st = check_shape(B, L, D, flags, fused != 0);
   if (st != RN_OK) return st;
-  const int vi = shape_for(B * L, D, flags, fused != 0, RN_DTYPE_BF16,
+  const int affine_dtype = ext ? ext->affine_dtype : RN_DTYPE_BF16;
+  if (affine_dtype != RN_DTYPE_BF16 && affine_dtype != RN_DTYPE_F32)
+    return fail(RN_EINVAL, "affine_dtype %d is not RN_DTYPE_BF16 or RN_DTYPE_F32", affine_dtype);
+  const int vi = shape_for(B * L, D, flags, fused != 0, affine_dtype,
                            hbm_streams(flags, fused != 0, gate_layout, ss_layout));
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
   const rn::Shape s = rn::kShapes[vi];
@@ -399,6 +403,11 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   info->block_threads = rn::kWaveSize * s.w * s.rpb;
   info->grid_blocks = (B * L + info->rows_per_block - 1) / info->rows_per_block;
   return RN_OK;
+}
+
+rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
+                             rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info) {
+  return rn_describe_launch_ex(B, L, D, flags, fused, gate_layout, ss_layout, nullptr, info);
 }
 
 const char* rn_version(void) { return "resnorm 0.2.0 gfx950"; }

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("resnorm_fused_fwd", "norm_scale_shift_fwd", "rn_last_error",
-              "rn_describe_launch", "rn_version"):
+              "rn_describe_launch", "rn_describe_launch_ex", "rn_version"):
         assert n in names, names
 
 
@@ -207,6 +207,20 @@ def test_describe_launch(rn):
     assert fplan(512, 5120) == (4, 3) and fplan(513, 5120) == (1, 10)
     assert fplan(1024, 5120) == (1, 10) and fplan(1025, 5120) == (2, 5)
     assert fplan(768, 6144) == (4, 3)
+    # binary32 weight/bias count twice against the register budget
+    wb = rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS
+    a16 = rn.describe_launch(1, 176400, 5120, wb, True)
+    a32 = rn.describe_launch(1, 176400, 5120, wb, True, affine_dtype=rn.RN_DTYPE_F32)
+    assert (a16["waves_per_row"], a16["vec_per_lane"]) == (2, 5)
+    assert (a32["waves_per_row"], a32["vec_per_lane"]) == (2, 5)
+    # fused + gate + weight + bias at D = 3072: 7 (bf16) or 9 (binary32)
+    # operand vectors per VPT; one wave per row needs VPT 6
+    f16 = rn.describe_launch(1, 176400, 3072, wb, True)
+    f32 = rn.describe_launch(1, 176400, 3072, wb, True, affine_dtype=rn.RN_DTYPE_F32)
+    assert (f16["waves_per_row"], f16["vec_per_lane"]) == (1, 6)
+    assert (f32["waves_per_row"], f32["vec_per_lane"]) == (2, 3)
+    with pytest.raises(rn.RnError):
+        rn.describe_launch(1, 16, 5120, 0, False, affine_dtype=7)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3
     for D in range(8, 16385, 8):
         for fused, flags, gl, sl in ((False, 0, (0, 0), (0, 0)), (True, 14, (1, 0), (1, 0))):

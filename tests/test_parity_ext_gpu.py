@@ -222,7 +222,8 @@ def test_random_matrix(rn, orc):
         flags = (rn.RN_RMS if c["rms"] else 0) | (rn.RN_WEIGHT if c["aff"] else 0) | \
             (rn.RN_BIAS if c["aff"] in (2, 4) else 0) | (rn.RN_GATE if c["gate_layout"] else 0)
         info = rn.describe_launch(c["B"], c["L"], c["D"], flags, c["fused"],
-                                  c["gate_layout"] or (BCAST, 0), c["ss_layout"])
+                                  c["gate_layout"] or (BCAST, 0), c["ss_layout"],
+                                  rn.RN_DTYPE_F32 if c["aff"] in (3, 4) else rn.RN_DTYPE_BF16)
         seen.add(info["waves_per_row"])
         log("random case %d: %s" % (k, c))
         _run(rn, orc, 1000 + k, c["fused"], c["rms"], c["gate_layout"], c["aff"], c["ss_layout"],
