@@ -382,3 +382,30 @@ def test_header_is_plain_c_and_links(rn, tmp_path):
     assert lines[0] == "1 10 4 44100"
     assert "NULL" in lines[1]
     assert "y_scale" in lines[2]
+
+
+def test_last_error_is_per_thread(rn):
+    """rn_last_error() is thread-local: threads that fail with different
+    errors at the same time each read back their own message (ctypes releases
+    the GIL around the calls, so the C calls do interleave)."""
+    import threading
+    cases = [(dict(D=12), "multiple of 8"), (dict(D=20000), "RN_D_MAX"), (dict(eps=-1.0), "eps"),
+             (dict(flags=1 << 9), "unknown flag"), (dict(B=-1), "negative shape"),
+             (dict(y=addr(0) + 4), "16-byte aligned")]
+    errors = []
+    start = threading.Barrier(len(cases))
+
+    def worker(kw, want):
+        start.wait()
+        for _ in range(2000):
+            st, msg = nss(rn, **kw)
+            if st == 0 or want not in msg:
+                errors.append((kw, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
