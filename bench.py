@@ -178,6 +178,16 @@ def extras(rn, dev_tensors, steps, warmup):
     def nss_bcast():
         rn.norm_scale_shift_fwd(y, x, None, None, bc["scale"], bc["shift"], 1, R, D, 0, BC, 1e-6)
 
+    w16, b16 = w32.to(torch.bfloat16), b32.to(torch.bfloat16)
+
+    def nss_affine():
+        rn.norm_scale_shift_fwd_ex(y, x, w32, b32, bc["scale"], bc["shift"], 1, R, D, W | Bi, BC,
+                                   1e-6, F32)
+
+    def nss_affine_bf16():
+        rn.norm_scale_shift_fwd(y, x, w16, b16, bc["scale"], bc["shift"], 1, R, D, W | Bi, BC,
+                                1e-6)
+
     def frame_fp8():
         rn.resnorm_fused_fwd_ex(y8, ro, x, res, d["gate"], None, None, d["scale"], d["shift"],
                                 1, R, D, G, FR, FR, 1e-6, y_dtype=FP8, y_scale=ys)
@@ -204,6 +214,10 @@ def extras(rn, dev_tensors, steps, warmup):
          3 * act + 2 * act + 3 * 49 * row),
         ("fused_ln_per_batch_b4", "fused LN, B 4 x L 44100, (B,1,C) modulation", per_batch,
          4 * act + 3 * 4 * row),
+        ("nss_ln_bcast_affine_fp32", "norm-only LN + fp32 weight/bias, (1,C) modulation",
+         nss_affine, 2 * act + 2 * row + 2 * 4 * D),
+        ("nss_ln_bcast_affine_bf16", "norm-only LN + bf16 weight/bias, (1,C) modulation",
+         nss_affine_bf16, 2 * act + 4 * row),
     ]
     out = []
     for name, what, fn, nbytes in cases:
@@ -230,7 +244,7 @@ def extras(rn, dev_tensors, steps, warmup):
                      "fused, no affine": 40},
            "shape": "B 1, L 176400, D 5120, broadcast (1,C) gate/scale/shift, LayerNorm",
            "pages_prior_art_ms_per_forward_context": [171.6, 174.8]}
-    del y32, y8, ys, bc, pb, w32, b32
+    del y32, y8, ys, bc, pb, w32, b32, w16, b16
     return out, mix
 
 

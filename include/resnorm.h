@@ -166,15 +166,20 @@ const char* rn_last_error(void);
 
 /* Launch shape the library would use for a problem (host-only query; no
  * device work, usable without a GPU): 16-byte vectors per lane and operand,
- * waves per activation row, waves and rows per workgroup, workgroup size and
+ * waves per activation row, waves and rows per workgroup, workgroup size,
  * the number of workgroups (laid out over a second grid dimension when one
- * dimension would exceed 2^32 - 1 work-items).  `fused` selects resnorm_fused_fwd (1) or norm_scale_shift_fwd
- * (0); the layouts matter because per-row modulation operands add HBM
- * streams, which changes the preferred shape, and so does the row count
- * (small problems are latency-bound).  The answer is for bf16 weight/bias;
- * rn_describe_launch_ex takes the element types of the *_ex entry points
- * (binary32 weight/bias hold twice the registers per vector and may get a
- * shorter per-wave span; the output type does not change the shape). */
+ * dimension would exceed 2^32 - 1 work-items), and the consecutive rows
+ * each wave handles in turn (1, or 4 for the norm-only op with weight
+ * from 12 Mi elements (B * L * D >= 12582912) when every aligned group of 4
+ * rows shares its scale/shift row: the wave then loads weight, bias, scale
+ * and shift once for its 4 rows).  `fused` selects resnorm_fused_fwd (1) or
+ * norm_scale_shift_fwd (0); the layouts matter because per-row modulation
+ * operands add HBM streams, which changes the preferred shape, and so does
+ * the row count (small problems are latency-bound).  The answer is for bf16
+ * weight/bias; rn_describe_launch_ex takes the element types of the *_ex
+ * entry points (binary32 weight/bias hold twice the registers per vector
+ * and may get a shorter per-wave span; the output type does not change the
+ * shape). */
 typedef struct {
   int32_t vec_per_lane;
   int32_t waves_per_row;
@@ -182,6 +187,7 @@ typedef struct {
   int32_t rows_per_block;
   int32_t block_threads;
   int64_t grid_blocks;
+  int32_t rows_per_wave;
 } rn_launch_info;
 
 rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,

@@ -50,7 +50,7 @@ class rn_launch_info(ctypes.Structure):
     _fields_ = [("vec_per_lane", ctypes.c_int32), ("waves_per_row", ctypes.c_int32),
                 ("waves_per_block", ctypes.c_int32),
                 ("rows_per_block", ctypes.c_int32), ("block_threads", ctypes.c_int32),
-                ("grid_blocks", ctypes.c_int64)]
+                ("grid_blocks", ctypes.c_int64), ("rows_per_wave", ctypes.c_int32)]
 
 
 class RnError(RuntimeError):

@@ -120,6 +120,16 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
   return n;
 }
 
+// Whether every aligned group of k consecutive rows (rows k*m .. k*m + k - 1)
+// shares one scale/shift row: always for a broadcast row, for per-frame rows
+// when the frame length is a multiple of k (frames tile each batch, so the
+// batch length is one too), never for per-row operands.
+bool groups_share_ss(rn_layout ss, int64_t L, int k) {
+  if (ss.kind == RN_BCAST) return true;
+  if (ss.kind != RN_FRAME || ss.frames < 1 || L % ss.frames != 0) return false;
+  return (L / ss.frames) % k == 0;
+}
+
 // The compiled shape for a problem (see kShapes); -1 if none covers D.
 // Waves per row the planner aims for (0: the first compiled shape with W < 10
 // that fits the register budget); the measurements behind each rule are
@@ -136,25 +146,34 @@ int preferred_waves(int64_t R, int64_t D, int streams, bool fused, bool one_wave
   return 0;
 }
 
-int shape_for(int64_t R, int64_t D, uint32_t flags, bool fused, int affine_dtype, int streams) {
+int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int affine_dtype,
+              int streams, rn_layout ss_layout) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
   auto covers = [&](const rn::Shape& s) { return (int64_t)rn::kWaveSize * s.w * s.vpt >= nvec; };
+  if (!fused && (flags & RN_WEIGHT) && R * D >= rn::kMultiRowMinElems) {
+    for (int i = 0; i < rn::kNumShapes; ++i) {
+      const rn::Shape s = rn::kShapes[i];
+      if (s.k > 1 && covers(s) && groups_share_ss(ss_layout, L, s.k)) return i;
+    }
+  }
   bool one_wave_fits = false;
   for (int i = 0; i < rn::kNumShapes; ++i)
-    one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && covers(rn::kShapes[i]) &&
+    one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && rn::kShapes[i].k == 1 &&
+                                      covers(rn::kShapes[i]) &&
                                       rn::kShapes[i].vpt * ops <= rn::kVgprBudget);
   const int want = preferred_waves(R, D, streams, fused, one_wave_fits);
   if (want != 0) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
-      if (s.w == want && covers(s) && (want == 10 || s.vpt * ops <= rn::kVgprBudget)) return i;
+      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || s.vpt * ops <= rn::kVgprBudget))
+        return i;
     }
   }
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
-    if (s.w == 10 || !covers(s)) continue;
+    if (s.k > 1 || s.w == 10 || !covers(s)) continue;
     if (s.vpt * ops <= rn::kVgprBudget) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
@@ -260,8 +279,8 @@ rn_status run(const Problem& p, void* stream) {
   if (st != RN_OK) return st;
   const int64_t R = p.B * p.L;
   if (R == 0) return RN_OK;
-  const int vi = shape_for(R, p.D, p.flags, p.fused, p.affine_dtype,
-                           hbm_streams(p.flags, p.fused, p.gate_layout, p.ss_layout));
+  const int vi = shape_for(R, p.L, p.D, p.flags, p.fused, p.affine_dtype,
+                           hbm_streams(p.flags, p.fused, p.gate_layout, p.ss_layout), p.ss_layout);
   rn::KernelFn fn = vi < 0 ? nullptr : pick_kernel(p, vi);
   if (!fn) return fail(RN_EUNSUPPORTED, "no compiled kernel for D=%lld flags=0x%x", (long long)p.D, p.flags);
 
@@ -290,7 +309,8 @@ rn_status run(const Problem& p, void* stream) {
   if (!(p.flags & RN_GATE)) a.gate_kind = RN_BCAST;
 
   const rn::Shape shape = rn::kShapes[vi];
-  const int64_t blocks = (R + shape.rpb - 1) / shape.rpb;
+  const int64_t rows_per_block = (int64_t)shape.rpb * shape.k;
+  const int64_t blocks = (R + rows_per_block - 1) / rows_per_block;
   const int64_t threads = (int64_t)rn::kWaveSize * shape.w * shape.rpb;
   // A dispatch counts work-items per grid dimension in 32 bits: beyond that
   // the workgroups continue in y (the kernel numbers them x-fastest; the
@@ -392,16 +412,17 @@ rn_status rn_describe_launch_ex(int64_t B, int64_t L, int64_t D, uint32_t flags,
   const int affine_dtype = ext ? ext->affine_dtype : RN_DTYPE_BF16;
   if (affine_dtype != RN_DTYPE_BF16 && affine_dtype != RN_DTYPE_F32)
     return fail(RN_EINVAL, "affine_dtype %d is not RN_DTYPE_BF16 or RN_DTYPE_F32", affine_dtype);
-  const int vi = shape_for(B * L, D, flags, fused != 0, affine_dtype,
-                           hbm_streams(flags, fused != 0, gate_layout, ss_layout));
+  const int vi = shape_for(B * L, L, D, flags, fused != 0, affine_dtype,
+                           hbm_streams(flags, fused != 0, gate_layout, ss_layout), ss_layout);
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);
   const rn::Shape s = rn::kShapes[vi];
   info->vec_per_lane = s.vpt;
   info->waves_per_row = s.w;
   info->waves_per_block = s.w * s.rpb;
-  info->rows_per_block = s.rpb;
+  info->rows_per_block = s.rpb * s.k;
   info->block_threads = rn::kWaveSize * s.w * s.rpb;
   info->grid_blocks = (B * L + info->rows_per_block - 1) / info->rows_per_block;
+  info->rows_per_wave = s.k;
   return RN_OK;
 }
 
@@ -410,6 +431,6 @@ rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, in
   return rn_describe_launch_ex(B, L, D, flags, fused, gate_layout, ss_layout, nullptr, info);
 }
 
-const char* rn_version(void) { return "resnorm 0.2.0 gfx950"; }
+const char* rn_version(void) { return "resnorm 0.3.0 gfx950"; }
 
 }  // extern "C"

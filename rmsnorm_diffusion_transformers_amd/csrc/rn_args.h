@@ -37,18 +37,40 @@ constexpr int kWaveSize = 64;
 //   * the fused op keeps one wave per row (when it fits the register budget)
 //     from 2 * kSmallRows + 1 up to kFusedOneWaveRows rows: with its loads
 //     ordered, spaced and prioritised it measured 5-18 % faster there than
-//     2 or 4 waves per row (e.g. D = 5120, 1024 rows: 9.8 -> 8.3 us).
+//     2 or 4 waves per row (e.g. D = 5120, 1024 rows: 9.8 -> 8.3 us);
+//   * the norm-only op with weight (and bias), from kMultiRowMinElems
+//     elements (rows x D), when every aligned group of K rows shares one
+//     scale/shift row, runs a multi-row shape (K > 1): each wave loads the
+//     shared rows -- weight, bias, scale, shift -- once and then streams K
+//     consecutive rows through them, instead of re-reading up to 60 KB of
+//     shared rows from L2 for every 10 KB activation row.  The first
+//     multi-row shape that covers D (at most 5 vectors per lane, so the
+//     shared rows stay in registers at 2 waves per SIMD) measured faster
+//     than the one-row shapes at every point of a sweep from 12.6 M
+//     elements up, D = 512 to 10240, by 0.5-66 % (D = 5120, L = 176400:
+//     binary32 weight/bias 0.69 -> 0.61 ms, bf16 0.92 -> 0.61 ms), and
+//     slower below about 8 M elements, where 4x fewer waves leave part of
+//     the chip idle.  K = 4 beat K = 2 and
+//     K = 8; prefetching the next row before the current row's stores did
+//     not help on balance.  The fused op and the norm-only op without
+//     affine ran slower as multi-row shapes.
 struct Shape {
   int w;
   int vpt;
   int rpb;
+  int k = 1;  // consecutive rows per wave
 };
-// Sorted by W, then VPT: the planner takes the first fit of a given W.
+// One-row shapes sorted by W, then VPT (the planner takes the first fit of a
+// given W), then the multi-row shapes in the same order.
 constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1, 5, 4},
                              {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 3, 2},  {2, 4, 2},
                              {2, 5, 2},  {2, 6, 2},  {2, 8, 2},  {2, 10, 2}, {4, 2, 1},
                              {4, 3, 1},  {4, 4, 1},  {4, 5, 1},  {4, 6, 1},  {4, 8, 1},
-                             {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1}};
+                             {10, 1, 1}, {10, 2, 1}, {10, 3, 1}, {10, 4, 1},
+                             // multi-row shapes (norm-only with weight)
+                             {1, 1, 4, 4}, {1, 2, 4, 4}, {1, 3, 4, 4}, {1, 4, 4, 4},
+                             {1, 5, 4, 4}, {2, 3, 2, 4}, {2, 4, 2, 4}, {2, 5, 2, 4},
+                             {4, 3, 1, 4}, {4, 4, 1, 4}, {4, 5, 1, 4}};
 constexpr int kManyStreamsMinD = 2560;
 constexpr int kSplitMinD = 2048;
 constexpr int kTinyRows = 128;
@@ -56,6 +78,7 @@ constexpr int kSmallRows = 256;
 constexpr int kMidRowsSplit4 = 768;
 constexpr int kMidRows = 1536;
 constexpr int kFusedOneWaveRows = 1024;
+constexpr int64_t kMultiRowMinElems = 12 << 20;
 constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // VPT x operands per row kept below this: all loads of a row are in flight at
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough

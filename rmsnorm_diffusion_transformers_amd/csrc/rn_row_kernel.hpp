@@ -12,8 +12,11 @@
 //   y            = bf16(n * (1 + scale) + shift)
 //
 // Design (HBM-bound; no matrix cores -- nothing here is a contraction):
-//   * W wave64s own one activation row and a workgroup holds RPB rows
-//     (W * RPB waves).  Row indices are wave-uniform, so per-row quantities
+//   * W wave64s own one activation row and a workgroup holds RPB row slots
+//     (W * RPB waves).  A slot takes K consecutive rows in turn (K = 1 for
+//     most shapes; 4 for the multi-row shapes, which load the rows shared by
+//     the K rows -- weight, bias, scale, shift -- once per wave instead of
+//     once per row).  Row indices are wave-uniform, so per-row quantities
 //     (descriptors, modulation row, statistics) live in SGPRs.
 //   * Every global access is a 128-bit buffer load/store (8 bf16 per lane) on
 //     a per-row buffer descriptor whose range is exactly the row: lanes past
@@ -240,12 +243,23 @@ struct AffineRow {
   }
 };
 
+// Position of one activation row: its index (0 past the last row), its byte
+// offset, and the byte range of its buffers (0 past the last row, which
+// turns every access into a no-op).
+struct RowPos {
+  uint32_t r;
+  uint32_t bytes;
+  uint64_t off;
+  bool live;
+};
+
 template <class OP, int SHAPE>
 __global__ __launch_bounds__(kWaveSize * kShapes[SHAPE].w * kShapes[SHAPE].rpb)
 void row_kernel(const RowArgs a) {
   constexpr int W = kShapes[SHAPE].w;
   constexpr int VPT = kShapes[SHAPE].vpt;
   constexpr int RPB = kShapes[SHAPE].rpb;
+  constexpr int K = kShapes[SHAPE].k;
   constexpr int PL = kPaceLoads;
   constexpr int PS = OP::out == kOutF32 ? kPaceStoresF32 : kPaceStores;
   static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
@@ -259,46 +273,54 @@ void row_kernel(const RowArgs a) {
   const uint32_t part = wave % W;  // which contiguous part of the row this wave holds
   // Workgroups are numbered x-fastest over a 2D grid: the dispatch counts
   // work-items per dimension in 32 bits, so large problems spill into y.
-  const uint32_t row = (blockIdx.y * gridDim.x + blockIdx.x) * RPB + slot;
+  // A row slot holds K consecutive rows, the first at `first`.
+  const uint32_t first = ((blockIdx.y * gridDim.x + blockIdx.x) * RPB + slot) * K;
   // With W > 1 every wave must reach the barriers, so a wave past the last
   // row keeps going with its memory operations disabled (zero-range buffers).
-  const bool live = row < a.rows;
+  auto at = [&](uint32_t row) {
+    RowPos p;
+    p.live = row < a.rows;
+    p.bytes = p.live ? a.d * 2u : 0u;
+    p.r = p.live ? row : 0u;
+    p.off = (uint64_t)p.r * (a.d * 2u);
+    return p;
+  };
   if constexpr (W == 1) {
-    if (!live) return;
+    if (first >= a.rows) return;
   }
-  const uint32_t row_bytes = live ? a.d * 2u : 0u;
-  const uint32_t r = live ? row : 0u;
-  const uint64_t row_off = (uint64_t)r * (a.d * 2u);
-  const uint32_t b = r / a.L;
-  const uint32_t l = r - b * a.L;
-  const uint32_t srow = mod_row(a.ss_kind, a.ss_frames, a.ss_tokens_per_frame, r, b, l);
+  const RowPos p0 = at(first);
+  // Modulation rows of the slot's first row; with K > 1 the host guarantees
+  // that all K rows share them.
+  const uint32_t b = p0.r / a.L;
+  const uint32_t l = p0.r - b * a.L;
+  const uint32_t srow = mod_row(a.ss_kind, a.ss_frames, a.ss_tokens_per_frame, p0.r, b, l);
   // lane-local byte offset of vector v (bf16): this wave's part, then 1 KB per vector
   const uint32_t base = (part * VPT * kWaveSize + lane) * 16u;
 
-  const auto rs_x = row_rsrc((const char*)a.x + row_off, row_bytes);
-  const auto rs_sc = row_rsrc((const char*)a.scale + (uint64_t)srow * (a.d * 2u), row_bytes);
-  const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * (a.d * 2u), row_bytes);
+  const auto rs_sc = row_rsrc((const char*)a.scale + (uint64_t)srow * (a.d * 2u), p0.bytes);
+  const auto rs_sh = row_rsrc((const char*)a.shift + (uint64_t)srow * (a.d * 2u), p0.bytes);
 
-  // ---- every load of the row, before any store ----
+  // ---- every load of a row, before any store ----
   // The order of the groups of loads is fixed at compile time (a run-time
   // choice merges paths whose loads are counted in different orders, and
-  // the waits after the merge then cover every load).  Measured on MI355X
-  // at L = 90000-176400 (1-5 % on the whole kernel): ten waves per row (the
-  // shapes chosen when per-row scale/shift or gate are streamed from HBM):
-  // the activation rows, gate, weight/bias, scale/shift; otherwise the
-  // shared rows ahead of the activation rows -- without affine: gate,
-  // scale/shift, activation rows; with affine: scale/shift, activation
-  // rows, gate, weight/bias.
+  // the waits after the merge then cover every load).  One row per slot,
+  // measured on MI355X at L = 90000-176400 (1-5 % on the whole kernel): ten
+  // waves per row (the shapes chosen when per-row scale/shift or gate are
+  // streamed from HBM): the activation rows, gate, weight/bias,
+  // scale/shift; otherwise the shared rows ahead of the activation rows --
+  // without affine: gate, scale/shift, activation rows; with affine:
+  // scale/shift, activation rows, gate, weight/bias.  Several rows per
+  // slot: the shared rows once, then each row's activation rows.
   u32x4 h[VPT];  // x (norm-only) or residual, later the bf16-packed residual_out
   [[maybe_unused]] u32x4 xv[VPT];
   [[maybe_unused]] u32x4 gv[VPT];
   [[maybe_unused]] AffineRow<OP::aff32, VPT> wv, bv;
   u32x4 sc[VPT], sh[VPT];
-  const uint32_t aff_bytes = live ? a.d * (OP::aff32 ? 4u : 2u) : 0u;
+  const uint32_t aff_bytes = p0.live ? a.d * (OP::aff32 ? 4u : 2u) : 0u;
   auto load_gate = [&]() {
     if constexpr (OP::fused && OP::gate) {
-      const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, r, b, l);
-      const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * (a.d * 2u), row_bytes);
+      const uint32_t grow = mod_row(a.gate_kind, a.gate_frames, a.gate_tokens_per_frame, p0.r, b, l);
+      const auto rs_g = row_rsrc((const char*)a.gate + (uint64_t)grow * (a.d * 2u), p0.bytes);
 #pragma unroll
       for (int v = 0; v < VPT; ++v) gv[v] = load16<kPolicyDefault, PL>(rs_g, base + v * 1024u);
     }
@@ -315,13 +337,14 @@ void row_kernel(const RowArgs a) {
     if constexpr (OP::has_w) wv.template load<PL>(row_rsrc(a.weight, aff_bytes), base);
     if constexpr (OP::has_b) bv.template load<PL>(row_rsrc(a.bias, aff_bytes), base);
   };
-  auto load_rows = [&]() {
+  auto load_rows = [&](const RowPos& p) {
+    const auto rs_x = row_rsrc((const char*)a.x + p.off, p.bytes);
     if constexpr (OP::fused) {
       // the fused op's 2 x VPT streamed loads, spaced (one wave per row):
       // measured 1 % faster at L = 176400, D = 5120; the norm-only op's VPT
       // loads run best unspaced
       constexpr int PLR = W == 1 ? kPaceFusedRowLoads : PL;
-      const auto rs_r = row_rsrc((const char*)a.residual + row_off, row_bytes);
+      const auto rs_r = row_rsrc((const char*)a.residual + p.off, p.bytes);
 #pragma unroll
       for (int v = 0; v < VPT; ++v) xv[v] = load16<kPolicyStream, PLR>(rs_x, base + v * 1024u);
 #pragma unroll
@@ -339,255 +362,292 @@ void row_kernel(const RowArgs a) {
     if (a.ss_kind == 1) load_ss(std::integral_constant<int, kPolicyStream>{});
     else load_ss(std::integral_constant<int, kPolicyDefault>{});
   };
-  // With one wave per row, a wave issues its loads at raised priority, so
-  // that the SIMD's other wave (busy with arithmetic or stores) does not
-  // delay them: measured ~1 % on the norm-only op, neutral on the fused one.
-  // Not with several waves per row: there it delays the row's other waves
-  // at the barriers (-12 % measured with binary32 weight/bias).
-  if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
-  if constexpr (W == 10) {
-    load_rows();
-    load_gate();
-    load_affine();
-    load_ss_any();
-  } else if constexpr (OP::has_w) {
-    load_ss_any();
-    load_rows();
-    load_gate();
-    load_affine();
-  } else {
-    load_gate();
-    load_ss_any();
-    load_rows();
-  }
-  if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
-
-  // ---- residual update (fused) ----
-  if constexpr (OP::fused) {
-    const auto rs_ro = row_rsrc((const char*)a.residual_out + row_off, row_bytes);
+  // ---- the rest of a row, once its loads are issued ----
+  auto process = [&](const RowPos& p) __attribute__((always_inline)) {
+    // ---- residual update (fused) ----
+    if constexpr (OP::fused) {
+      const auto rs_ro = row_rsrc((const char*)a.residual_out + p.off, p.bytes);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      u32x4 o;
+      for (int v = 0; v < VPT; ++v) {
+        u32x4 o;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float s0, s1;
-        if constexpr (OP::gate) {
-          // gate * x is exact in binary32 (8-bit x 8-bit significands), so the
-          // fused multiply-add rounds exactly once, like residual + (gate * x).
-          s0 = __builtin_fmaf(lo_f32(gv[v][j]), lo_f32(xv[v][j]), lo_f32(h[v][j]));
-          s1 = __builtin_fmaf(hi_f32(gv[v][j]), hi_f32(xv[v][j]), hi_f32(h[v][j]));
-        } else {
-          s0 = lo_f32(h[v][j]) + lo_f32(xv[v][j]);
-          s1 = hi_f32(h[v][j]) + hi_f32(xv[v][j]);
+        for (int j = 0; j < 4; ++j) {
+          float s0, s1;
+          if constexpr (OP::gate) {
+            // gate * x is exact in binary32 (8-bit x 8-bit significands), so the
+            // fused multiply-add rounds exactly once, like residual + (gate * x).
+            s0 = __builtin_fmaf(lo_f32(gv[v][j]), lo_f32(xv[v][j]), lo_f32(h[v][j]));
+            s1 = __builtin_fmaf(hi_f32(gv[v][j]), hi_f32(xv[v][j]), hi_f32(h[v][j]));
+          } else {
+            s0 = lo_f32(h[v][j]) + lo_f32(xv[v][j]);
+            s1 = hi_f32(h[v][j]) + hi_f32(xv[v][j]);
+          }
+          o[j] = pack_bf16(s0, s1);
         }
-        o[j] = pack_bf16(s0, s1);
+        store16<kPolicyStream, PS>(o, rs_ro, base + v * 1024u);
+        h[v] = o;
       }
-      store16<kPolicyStream, PS>(o, rs_ro, base + v * 1024u);
-      h[v] = o;
     }
-  }
 
-  // ---- statistics (fp32) ----
-  const float inv_d = 1.0f / (float)a.d;
-  float mean = 0.f;
-  float sq = 0.f;
-  if constexpr (!OP::rms) {
-    float sum = 0.f;
+    // ---- statistics (fp32) ----
+    const float inv_d = 1.0f / (float)a.d;
+    float mean = 0.f;
+    float sq = 0.f;
+    if constexpr (!OP::rms) {
+      float sum = 0.f;
 #pragma unroll
-    for (int v = 0; v < VPT; ++v)
+      for (int v = 0; v < VPT; ++v)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
-    mean = row_reduce<W>(sum, Add{}, red_sum, wave, slot) / (float)a.d;
-    // Finite values summing beyond the binary32 range (|h| ~ 1e34 and more):
-    // the mean again from h * 2^-k, k from the row's largest magnitude (a
-    // power of two, exact for every element that stays inside the binary32
-    // range; the others are negligible next to the largest), scaled back.
-    // Done before the variance pass, so that pass and the epilogue share
-    // the centred values.  A row holding an infinity or a NaN keeps its
-    // non-finite mean.
-    if (overflowed<W, RPB>(mean, red_sum)) {
+        for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
+      mean = row_reduce<W>(sum, Add{}, red_sum, wave, slot) / (float)a.d;
+      // Finite values summing beyond the binary32 range (|h| ~ 1e34 and more):
+      // the mean again from h * 2^-k, k from the row's largest magnitude (a
+      // power of two, exact for every element that stays inside the binary32
+      // range; the others are negligible next to the largest), scaled back.
+      // Done before the variance pass, so that pass and the epilogue share
+      // the centred values.  A row holding an infinity or a NaN keeps its
+      // non-finite mean.
+      if (overflowed<W, RPB>(mean, red_sum)) {
+        float m = 0.f;
+        const MaxNaN mx;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            m = mx(m, mx(__builtin_fabsf(lo_f32(h[v][j])), __builtin_fabsf(hi_f32(h[v][j]))));
+        m = row_reduce<W>(m, mx, red_max, wave, slot);
+        const int k = __builtin_isfinite(mean) ? 0 : scale_exp(m);
+        const float s = __builtin_ldexpf(1.0f, -k);
+        float sum2 = 0.f;
+#pragma unroll
+        for (int v = 0; v < VPT; ++v)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sum2 += lo_f32(h[v][j]) * s + hi_f32(h[v][j]) * s;
+        const float mean2 = row_reduce<W>(sum2, Add{}, red_sum, wave, slot) / (float)a.d;
+        if (k != 0) mean = __builtin_ldexpf(mean2, k);
+      }
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        float part_sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float d0 = lo_f32(h[v][j]) - mean;
+          const float d1 = hi_f32(h[v][j]) - mean;
+          part_sq = __builtin_fmaf(d0, d0, part_sq);
+          part_sq = __builtin_fmaf(d1, d1, part_sq);
+        }
+        // lanes past the end of a ragged row hold zeros, which are not zero
+        // after centring: leave them out.
+        sq += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPT; ++v)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float h0 = lo_f32(h[v][j]);
+          const float h1 = hi_f32(h[v][j]);
+          sq = __builtin_fmaf(h0, h0, sq);
+          sq = __builtin_fmaf(h1, h1, sq);
+        }
+    }
+    float var = row_reduce<W>(sq, Add{}, red_sq, wave, slot) * inv_d;
+    // Rounding can leave the variance slightly negative: lift it to 0.  A NaN
+    // variance (a row holding an infinity or a NaN) must stay NaN.
+    var = var < 0.f ? 0.f : var;
+    float rstd = __builtin_amdgcn_rsqf(var + a.eps);
+    // Finite centred values whose squares sum beyond the binary32 range
+    // (|h - mean| ~ 1e17-1e19 and more): the variance again from
+    // (h - mean) * 2^-k, k from the largest centred magnitude, and
+    // rstd = 2^-k / sqrt(var' + eps * 2^-2k).  Only rstd changes, so the
+    // epilogue is the same for every row.
+    if (overflowed<W, RPB>(var, red_sq)) {
       float m = 0.f;
       const MaxNaN mx;
 #pragma unroll
       for (int v = 0; v < VPT; ++v)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          m = mx(m, mx(__builtin_fabsf(lo_f32(h[v][j])), __builtin_fabsf(hi_f32(h[v][j]))));
+        for (int j = 0; j < 4; ++j) {
+          const bool in_row = base / 16u + (uint32_t)(v * kWaveSize) < a.nvec;
+          const float d0 = in_row ? __builtin_fabsf(lo_f32(h[v][j]) - mean) : 0.f;
+          const float d1 = in_row ? __builtin_fabsf(hi_f32(h[v][j]) - mean) : 0.f;
+          m = mx(m, mx(d0, d1));
+        }
       m = row_reduce<W>(m, mx, red_max, wave, slot);
-      const int k = __builtin_isfinite(mean) ? 0 : scale_exp(m);
+      const int k = __builtin_isfinite(var) ? 0 : scale_exp(m);
       const float s = __builtin_ldexpf(1.0f, -k);
-      float sum2 = 0.f;
+      float sq2 = 0.f;
 #pragma unroll
-      for (int v = 0; v < VPT; ++v)
+      for (int v = 0; v < VPT; ++v) {
+        float part_sq = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sum2 += lo_f32(h[v][j]) * s + hi_f32(h[v][j]) * s;
-      const float mean2 = row_reduce<W>(sum2, Add{}, red_sum, wave, slot) / (float)a.d;
-      if (k != 0) mean = __builtin_ldexpf(mean2, k);
+        for (int j = 0; j < 4; ++j) {
+          const float d0 = (lo_f32(h[v][j]) - mean) * s;
+          const float d1 = (hi_f32(h[v][j]) - mean) * s;
+          part_sq = __builtin_fmaf(d0, d0, part_sq);
+          part_sq = __builtin_fmaf(d1, d1, part_sq);
+        }
+        sq2 += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
+      }
+      float var2 = row_reduce<W>(sq2, Add{}, red_sq, wave, slot) * inv_d;
+      var2 = var2 < 0.f ? 0.f : var2;
+      if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
     }
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float part_sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float d0 = lo_f32(h[v][j]) - mean;
-        const float d1 = hi_f32(h[v][j]) - mean;
-        part_sq = __builtin_fmaf(d0, d0, part_sq);
-        part_sq = __builtin_fmaf(d1, d1, part_sq);
-      }
-      // lanes past the end of a ragged row hold zeros, which are not zero
-      // after centring: leave them out.
-      sq += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float h0 = lo_f32(h[v][j]);
-        const float h1 = hi_f32(h[v][j]);
-        sq = __builtin_fmaf(h0, h0, sq);
-        sq = __builtin_fmaf(h1, h1, sq);
-      }
-  }
-  float var = row_reduce<W>(sq, Add{}, red_sq, wave, slot) * inv_d;
-  // Rounding can leave the variance slightly negative: lift it to 0.  A NaN
-  // variance (a row holding an infinity or a NaN) must stay NaN.
-  var = var < 0.f ? 0.f : var;
-  float rstd = __builtin_amdgcn_rsqf(var + a.eps);
-  // Finite centred values whose squares sum beyond the binary32 range
-  // (|h - mean| ~ 1e17-1e19 and more): the variance again from
-  // (h - mean) * 2^-k, k from the largest centred magnitude, and
-  // rstd = 2^-k / sqrt(var' + eps * 2^-2k).  Only rstd changes, so the
-  // epilogue is the same for every row.
-  if (overflowed<W, RPB>(var, red_sq)) {
-    float m = 0.f;
-    const MaxNaN mx;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool in_row = base / 16u + (uint32_t)(v * kWaveSize) < a.nvec;
-        const float d0 = in_row ? __builtin_fabsf(lo_f32(h[v][j]) - mean) : 0.f;
-        const float d1 = in_row ? __builtin_fabsf(hi_f32(h[v][j]) - mean) : 0.f;
-        m = mx(m, mx(d0, d1));
-      }
-    m = row_reduce<W>(m, mx, red_max, wave, slot);
-    const int k = __builtin_isfinite(var) ? 0 : scale_exp(m);
-    const float s = __builtin_ldexpf(1.0f, -k);
-    float sq2 = 0.f;
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float part_sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float d0 = (lo_f32(h[v][j]) - mean) * s;
-        const float d1 = (hi_f32(h[v][j]) - mean) * s;
-        part_sq = __builtin_fmaf(d0, d0, part_sq);
-        part_sq = __builtin_fmaf(d1, d1, part_sq);
-      }
-      sq2 += (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? part_sq : 0.f;
-    }
-    float var2 = row_reduce<W>(sq2, Add{}, red_sq, wave, slot) * inv_d;
-    var2 = var2 < 0.f ? 0.f : var2;
-    if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
-  }
 
-  // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v
-  auto tval = [&](int v, int j, int k) -> float {
-    const float hv = k ? hi_f32(h[v][j]) : lo_f32(h[v][j]);
-    float n = (hv - mean) * rstd;
-    if constexpr (OP::has_w && OP::has_b) {
-      n = __builtin_fmaf(n, k ? wv.hi(v, j) : wv.lo(v, j), k ? bv.hi(v, j) : bv.lo(v, j));
-    } else if constexpr (OP::has_w) {
-      n *= k ? wv.hi(v, j) : wv.lo(v, j);
+    // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v
+    auto tval = [&](int v, int j, int k) -> float {
+      const float hv = k ? hi_f32(h[v][j]) : lo_f32(h[v][j]);
+      float n = (hv - mean) * rstd;
+      if constexpr (OP::has_w && OP::has_b) {
+        n = __builtin_fmaf(n, k ? wv.hi(v, j) : wv.lo(v, j), k ? bv.hi(v, j) : bv.lo(v, j));
+      } else if constexpr (OP::has_w) {
+        n *= k ? wv.hi(v, j) : wv.lo(v, j);
+      }
+      const float s = k ? hi_f32(sc[v][j]) : lo_f32(sc[v][j]);
+      const float t = k ? hi_f32(sh[v][j]) : lo_f32(sh[v][j]);
+      return __builtin_fmaf(n, 1.0f + s, t);
+    };
+
+    // ---- epilogue from the register cache ----
+    if constexpr (OP::out == kOutBf16) {
+      {
+        const auto rs_y = row_rsrc((const char*)a.y + p.off, p.bytes);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+          u32x4 o;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = pack_bf16(tval(v, j, 0), tval(v, j, 1));
+          store16<kPolicyStream, PS>(o, rs_y, base + v * 1024u);
+        }
+      }
+    } else if constexpr (OP::out == kOutF32) {
+      {
+        // binary32 y: 32 bytes per lane per vector, two 16-byte stores
+        const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)p.r * (a.d * 4u), p.live ? a.d * 4u : 0u);
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+          u32x4 o0, o1;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            o0[2 * j] = __float_as_uint(tval(v, j, 0));
+            o0[2 * j + 1] = __float_as_uint(tval(v, j, 1));
+            o1[2 * j] = __float_as_uint(tval(v, j + 2, 0));
+            o1[2 * j + 1] = __float_as_uint(tval(v, j + 2, 1));
+          }
+          // each store covers every other 16-byte chunk of a 2 KB span; the
+          // default policy lets L2 merge the pair into whole lines
+          store16<kPolicyDefault, PS>(o0, rs_y, base * 2u + v * 2048u);
+          store16<kPolicyDefault, PS>(o1, rs_y, base * 2u + v * 2048u + 16u);
+        }
+      }
+    } else {
+      // FP8 E4M3 y with a per-row scale: the row maximum of |t| first (lanes
+      // past a ragged row's end are left out), then t * 448 / max converted.
+      float amax = 0.f;
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(tval(v, j, 0)),
+                                                 __builtin_fabsf(tval(v, j, 1))));
+        amax = (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? __builtin_fmaxf(amax, m) : amax;
+      }
+      amax = row_reduce<W>(amax, Max{}, red_max, wave, slot);
+      const float inv = amax > 0.f ? 448.0f / amax : 0.f;
+      const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)p.r * a.d, p.live ? a.d : 0u);
+#pragma unroll
+      for (int v = 0; v < VPT; ++v) {
+        uint32_t w0 = 0, w1 = 0;
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 0, 0) * inv, tval(v, 0, 1) * inv, w0, false);
+        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 1, 0) * inv, tval(v, 1, 1) * inv, w0, true);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 2, 0) * inv, tval(v, 2, 1) * inv, w1, false);
+        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 3, 0) * inv, tval(v, 3, 1) * inv, w1, true);
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        __builtin_amdgcn_raw_buffer_store_b64((u32x2){w0, w1}, rs_y, base / 2u + v * 512u, 0,
+                                              kPolicyStream);
+        pace<PS>();
+      }
+      if (p.live && part == 0 && lane == 0) a.y_scale[p.r] = amax / 448.0f;
     }
-    const float s = k ? hi_f32(sc[v][j]) : lo_f32(sc[v][j]);
-    const float t = k ? hi_f32(sh[v][j]) : lo_f32(sh[v][j]);
-    return __builtin_fmaf(n, 1.0f + s, t);
   };
 
-  // ---- epilogue from the register cache ----
-  if constexpr (OP::out == kOutBf16) {
-    {
-      const auto rs_y = row_rsrc((const char*)a.y + row_off, row_bytes);
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[j] = pack_bf16(tval(v, j, 0), tval(v, j, 1));
-        store16<kPolicyStream, PS>(o, rs_y, base + v * 1024u);
-      }
+  if constexpr (K == 1) {
+    // With one wave per row, a wave issues its loads at raised priority, so
+    // that the SIMD's other wave (busy with arithmetic or stores) does not
+    // delay them: measured ~1 % on the norm-only op, neutral on the fused one.
+    // Not with several waves per row: there it delays the row's other waves
+    // at the barriers (-12 % measured with binary32 weight/bias).
+    if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
+    if constexpr (W == 10) {
+      load_rows(p0);
+      load_gate();
+      load_affine();
+      load_ss_any();
+    } else if constexpr (OP::has_w) {
+      load_ss_any();
+      load_rows(p0);
+      load_gate();
+      load_affine();
+    } else {
+      load_gate();
+      load_ss_any();
+      load_rows(p0);
     }
-  } else if constexpr (OP::out == kOutF32) {
-    {
-      // binary32 y: 32 bytes per lane per vector, two 16-byte stores
-      const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)r * (a.d * 4u), live ? a.d * 4u : 0u);
-#pragma unroll
-      for (int v = 0; v < VPT; ++v) {
-        u32x4 o0, o1;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          o0[2 * j] = __float_as_uint(tval(v, j, 0));
-          o0[2 * j + 1] = __float_as_uint(tval(v, j, 1));
-          o1[2 * j] = __float_as_uint(tval(v, j + 2, 0));
-          o1[2 * j + 1] = __float_as_uint(tval(v, j + 2, 1));
-        }
-        // each store covers every other 16-byte chunk of a 2 KB span; the
-        // default policy lets L2 merge the pair into whole lines
-        store16<kPolicyDefault, PS>(o0, rs_y, base * 2u + v * 2048u);
-        store16<kPolicyDefault, PS>(o1, rs_y, base * 2u + v * 2048u + 16u);
-      }
-    }
+    if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
+    process(p0);
   } else {
-    // FP8 E4M3 y with a per-row scale: the row maximum of |t| first (lanes
-    // past a ragged row's end are left out), then t * 448 / max converted.
-    float amax = 0.f;
+    // K consecutive rows share the slot's modulation rows and the affine
+    // rows: those are loaded once, then each row streams its own operands
+    // through them.
+    if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
+    load_ss_any();
+    load_gate();
+    load_affine();
+    if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      float m = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(tval(v, j, 0)),
-                                               __builtin_fabsf(tval(v, j, 1))));
-      amax = (base / 16u + (uint32_t)(v * kWaveSize) < a.nvec) ? __builtin_fmaxf(amax, m) : amax;
+    for (int k = 0; k < K; ++k) {
+      const RowPos p = at(first + (uint32_t)k);
+      if constexpr (W == 1) {
+        if (!p.live) break;
+      }
+      if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
+      load_rows(p);
+      if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
+      process(p);
     }
-    amax = row_reduce<W>(amax, Max{}, red_max, wave, slot);
-    const float inv = amax > 0.f ? 448.0f / amax : 0.f;
-    const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)r * a.d, live ? a.d : 0u);
-#pragma unroll
-    for (int v = 0; v < VPT; ++v) {
-      uint32_t w0 = 0, w1 = 0;
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 0, 0) * inv, tval(v, 0, 1) * inv, w0, false);
-      w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 1, 0) * inv, tval(v, 1, 1) * inv, w0, true);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 2, 0) * inv, tval(v, 2, 1) * inv, w1, false);
-      w1 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 3, 0) * inv, tval(v, 3, 1) * inv, w1, true);
-      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_amdgcn_raw_buffer_store_b64((u32x2){w0, w1}, rs_y, base / 2u + v * 512u, 0,
-                                            kPolicyStream);
-      pace<PS>();
-    }
-    if (live && part == 0 && lane == 0) a.y_scale[r] = amax / 448.0f;
   }
+}
+
+// Whether a shape is compiled for an operation: multi-row shapes only for
+// the norm-only op with weight, the one the planner gives them to.
+template <class OP, int SHAPE>
+constexpr bool compiled() {
+  return kShapes[SHAPE].k == 1 || (!OP::fused && OP::has_w);
 }
 
 // Table of one operation over every compiled shape.
 template <class OP>
 KernelFn kernel_for_shape(int shape) {
   switch (shape) {
-#define RN_CASE(i) \
-  case i:          \
-    return row_kernel<OP, i>;
+#define RN_CASE(i)                      \
+  case i:                               \
+    if constexpr (compiled<OP, i>())    \
+      return row_kernel<OP, i>;         \
+    else                                \
+      return nullptr;
     RN_CASE(0) RN_CASE(1) RN_CASE(2) RN_CASE(3) RN_CASE(4) RN_CASE(5) RN_CASE(6) RN_CASE(7)
     RN_CASE(8) RN_CASE(9) RN_CASE(10) RN_CASE(11) RN_CASE(12) RN_CASE(13) RN_CASE(14)
     RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18) RN_CASE(19) RN_CASE(20) RN_CASE(21)
-    RN_CASE(22) RN_CASE(23)
+    RN_CASE(22) RN_CASE(23) RN_CASE(24) RN_CASE(25) RN_CASE(26) RN_CASE(27) RN_CASE(28)
+    RN_CASE(29) RN_CASE(30) RN_CASE(31) RN_CASE(32) RN_CASE(33) RN_CASE(34)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumShapes == 24, "kernel_for_shape lists every shape");
+static_assert(kNumShapes == 35, "kernel_for_shape lists every shape");
 
 // Table of one (norm, op, gate, output) family over the affine variants.
 template <bool RMS, bool FUSED, bool GATE, int OUT>

@@ -231,6 +231,47 @@ def test_describe_launch(rn):
         rn.describe_launch(1, 3, 20000, 0, False)
 
 
+def test_describe_launch_multi_row(rn):
+    """The norm-only op with weight from 12 Mi elements: one wave streams 4
+    consecutive rows through weight, bias, scale and shift loaded once, on
+    the first multi-row shape that covers D (at most 5 vectors per lane),
+    when every aligned group of 4 rows shares its scale/shift row."""
+    W, WB = rn.RN_WEIGHT, rn.RN_WEIGHT | rn.RN_BIAS
+    def k_of(B, L, D, flags, fused=False, sl=(rn.RN_BCAST, 0), **kw):
+        i = rn.describe_launch(B, L, D, flags, fused, (rn.RN_BCAST, 0), sl, **kw)
+        return i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"]
+    i = rn.describe_launch(1, 176400, 5120, WB, False, affine_dtype=rn.RN_DTYPE_F32)
+    assert (i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"]) == (2, 5, 4)
+    assert i["rows_per_block"] == 8 and i["block_threads"] == 256
+    assert i["grid_blocks"] == 176400 // 8
+    assert k_of(1, 176400, 5120, W) == (2, 5, 4)
+    assert k_of(1, 441000, 2048, WB) == (1, 4, 4)
+    assert k_of(1, 294000, 3072, WB) == (2, 3, 4)
+    assert k_of(1, 110250, 8192, WB) == (4, 4, 4)
+    assert k_of(1, 90000, 10240, W) == (4, 5, 4)
+    assert k_of(1, 90000, 10248, W)[2] == 1          # no multi-row shape covers it
+    assert k_of(1, 786432, 16, W) == (1, 1, 4)
+    assert k_of(1, 786431, 16, W)[2] == 1
+    # not for the fused op, nor without weight, nor below 12 Mi elements
+    assert k_of(1, 176400, 5120, WB, True)[2] == 1
+    assert k_of(1, 176400, 5120, 0) == (1, 10, 1)
+    assert k_of(1, 2457, 5120, W)[2] == 1 and k_of(1, 2458, 5120, W)[2] == 4
+    assert k_of(2, 1229, 5120, W)[2] == 4 and k_of(3, 819, 5120, W)[2] == 1
+    # scale/shift rows shared by every aligned group of 4 rows
+    frame = lambda F: (rn.RN_FRAME, F)  # noqa: E731
+    assert k_of(1, 176400, 5120, W, sl=frame(49))[2] == 4      # 3600 tokens per frame
+    assert k_of(1, 176400, 5120, W, sl=frame(16))[2] == 1      # 11025 tokens per frame
+    assert k_of(2, 8196, 5120, W, sl=frame(1))[2] == 4          # per batch, L % 4 == 0
+    assert k_of(2, 8194, 5120, W, sl=frame(1))[2] == 1          # per batch, L % 4 == 2
+    assert k_of(1, 176400, 5120, W, sl=(rn.RN_ROW, 0))[2] == 1
+    assert k_of(1, 176400, 5120, W, sl=frame(0))[2] == 1        # invalid layout: no multi-row
+    for D in range(8, 10241, 8):
+        i = rn.describe_launch(1, -(-(12 << 20) // D), D, WB, False)
+        assert i["rows_per_wave"] == 4 and i["vec_per_lane"] <= 5
+        assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
+        assert i["rows_per_block"] == 4 * i["waves_per_block"] // i["waves_per_row"]
+
+
 def test_layout_inference(rn):
     import torch
     B, L, D = 2, 12, 16

@@ -212,6 +212,32 @@ def _random_cases(n, seed):
     return cases
 
 
+# Multi-row shapes (the norm-only op with weight on large problems): odd row
+# counts (a partly empty last workgroup), ragged rows, every W, affine and
+# output type, broadcast, per-frame (164 tokens per frame) and per-batch
+# scale/shift.  (B, L, D, aff, scale/shift layout, y dtype, rms, expected W)
+MULTI_ROW = [
+    (1, 12599, 1000, 4, (BCAST, 0), 0, False, 1),
+    (1, 12599, 1000, 1, (BCAST, 0), 2, True, 1),
+    (1, 8195, 3000, 2, (BCAST, 0), 1, True, 2),
+    (1, 8200, 5120, 4, (FRAME, 50), 0, False, 2),
+    (2, 4100, 5120, 3, (FRAME, 1), 2, False, 2),
+    (1, 8200, 9000, 3, (FRAME, 50), 1, False, 4),
+    (1, 8195, 9000, 2, (BCAST, 0), 0, True, 4),
+]
+
+
+@pytest.mark.parametrize("case", MULTI_ROW)
+def test_multi_row_shapes(rn, orc, case):
+    B, L, D, aff, sl, y_dtype, rms, w = case
+    flags = rn.RN_WEIGHT | (rn.RN_BIAS if aff in (2, 4) else 0) | (rn.RN_RMS if rms else 0)
+    info = rn.describe_launch(B, L, D, flags, False, (BCAST, 0), sl,
+                              affine_dtype=rn.RN_DTYPE_F32 if aff in (3, 4) else rn.RN_DTYPE_BF16)
+    assert (info["rows_per_wave"], info["waves_per_row"]) == (4, w)
+    log("multi-row: B=%d L=%d D=%d aff=%d ss=%s y=%d rms=%s" % case[:7])
+    _run(rn, orc, 1700 + D + aff, False, rms, None, aff, sl, B, L, D, y_dtype)
+
+
 def test_random_matrix(rn, orc):
     """120 seeded random problems through the _ex entry points against the
     oracle, each at the bar of its output type; the planner picks whatever
@@ -448,7 +474,8 @@ def test_maximum_row_count(rn, orc):
     """B * L = 2^31 - 1 rows (the largest the ABI accepts) at D = 8: 34 GB per
     tensor and a grid of 2^29 workgroups.  The inputs are a seeded block of
     65536 rows tiled over the tensor on the device; sampled rows (the first,
-    around 2^30, the last) against the oracle, for the norm-only op and the
+    around 2^30, the last) against the oracle, for the norm-only op, the
+    norm-only op with weight (four rows per wave, 2^27 workgroups) and the
     fused op (per-batch scale/shift, broadcast gate)."""
     D, T = 8, 65536
     L = (1 << 31) - 1
@@ -483,6 +510,17 @@ def test_maximum_row_count(rn, orc):
         xs = host_rows("x", r0, n)
         y_ref, _ = orc.nss(xs, None, None, sc, sh, 1, L, D, False, row0=r0, nrows=n)
         compare_outputs(to_host(y[r0:r0 + n]), y_ref, what="max rows nss at %d" % r0)
+    log("maximum rows: norm-only with weight (four rows per wave)")
+    w = synth.random_bf16((D,), 31, 4, a=1.0, b=0.05)
+    info_w = rn.describe_launch(1, L, D, rn.RN_WEIGHT, False)
+    assert info_w["rows_per_wave"] == 4
+    rn.norm_scale_shift_fwd(y, x, to_dev(w), None, dsc, dsh, 1, L, D, rn.RN_WEIGHT, (BCAST, 0),
+                            1e-6)
+    torch.cuda.synchronize()
+    for r0 in samples:
+        n = min(20, L - r0)
+        y_ref, _ = orc.nss(host_rows("x", r0, n), w, None, sc, sh, 1, L, D, False, row0=r0, nrows=n)
+        compare_outputs(to_host(y[r0:r0 + n]), y_ref, what="max rows nss+w at %d" % r0)
     del y
     log("maximum rows: fused")
     r = tiled("residual")
@@ -550,11 +588,13 @@ def test_two_dimensional_grid_ten_waves(rn, orc):
 def test_rescaled_statistics_ext_outputs(rn, orc):
     """Rows whose binary32 sums overflow (magnitudes 2^100 and 2^126), mixed
     with ordinary rows, with binary32 and FP8 outputs and binary32
-    weight/bias, on shapes with one, two, four and ten waves per row: the
+    weight/bias, on shapes with one, two, four and ten waves per row, and on
+    multi-row shapes (where a wave's consecutive rows mix the two kinds): the
     rescaled statistics and, for FP8, the row maximum that follows them in
     the same workgroup."""
     cases = [(5120, 2048, False, None, 0), (3072, 300, False, None, 0), (4096, 200, False, None, 0),
-             (2560, 64, True, (ROW, 0), 0), (5120, 600, True, (BCAST, 0), 4)]
+             (2560, 64, True, (ROW, 0), 0), (5120, 600, True, (BCAST, 0), 4),
+             (5120, 8195, False, None, 4), (1000, 12599, False, None, 2)]
     for k, (D, L, fused, gl, aff) in enumerate(cases):
         for y_dtype in (1, 2):
             inp = _problem(1500 + k, fused, gl, aff, (BCAST, 0), 1, L, D)
@@ -569,6 +609,6 @@ def test_rescaled_statistics_ext_outputs(rn, orc):
             flags = (rn.RN_GATE if gl is not None else 0) | \
                 (rn.RN_WEIGHT | rn.RN_BIAS if aff else 0)
             info = rn.describe_launch(1, L, D, flags, fused, gl or (BCAST, 0), (BCAST, 0))
-            log("rescaled statistics ext: D=%d L=%d fused=%s aff=%d y=%d W=%d" % (
-                D, L, fused, aff, y_dtype, info["waves_per_row"]))
+            log("rescaled statistics ext: D=%d L=%d fused=%s aff=%d y=%d W=%d K=%d" % (
+                D, L, fused, aff, y_dtype, info["waves_per_row"], info["rows_per_wave"]))
             _run_inputs(rn, orc, inp, fused, False, gl, aff, (BCAST, 0), 1, L, D, y_dtype)

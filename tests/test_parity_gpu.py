@@ -345,13 +345,15 @@ def test_mean_offset_rows(rn, orc):
 
 
 
-SHAPE_ROWS = ((2, 263), (2, 600), (2, 1031))   # a few hundred rows, a mid-size and a large problem
+# a few hundred rows, a mid-size and a large problem, and odd counts that
+# reach the multi-row threshold (12 Mi elements) from D = 1536 and D = 512
+SHAPE_ROWS = ((2, 263), (2, 600), (2, 1031), (1, 8195), (1, 24579))
 
 
 def _shape_cases(rn):
     """One (B, L, D, fused, flags, scale/shift layout) per compiled (waves per
-    row, vectors per lane) shape, at the first row count and row width that
-    select it."""
+    row, vectors per lane, rows per wave) shape, at the first row count and
+    row width that select it."""
     seen = {}
     flag_sets = [(False, 0), (True, rn.RN_GATE), (True, rn.RN_GATE | rn.RN_WEIGHT),
                  (True, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS), (False, rn.RN_WEIGHT | rn.RN_BIAS)]
@@ -361,25 +363,26 @@ def _shape_cases(rn):
                 for sl in ((BCAST, 0), (ROW, 0)):
                     gl = (FRAME, 1) if flags & rn.RN_GATE else (BCAST, 0)
                     i = rn.describe_launch(B, L, D, flags, fused, gl, sl)
-                    key = (i["waves_per_row"], i["vec_per_lane"])
+                    key = (i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"])
                     if key not in seen:
                         seen[key] = (B, L, D, fused, flags, sl)
     return seen
 
 
 def test_every_compiled_shape(rn, orc):
-    """Every compiled (waves per row, vectors per lane) shape the planner can
-    pick, at the first row width that selects it (a ragged row for most), with
-    odd L (so the last workgroup of a multi-row shape is partly empty)."""
+    """Every compiled (waves per row, vectors per lane, rows per wave) shape
+    the planner can pick, at the first row width that selects it (a ragged
+    row for most), with odd L (so the last workgroup of a shape with several
+    rows per workgroup is partly empty)."""
     cases = _shape_cases(rn)
-    assert len(cases) == 24, sorted(cases)
-    for (w, vpt), (B, L, D, fused, flags, sl) in sorted(cases.items()):
-        log("shape W=%d VPT=%d via B=%d L=%d D=%d fused=%s flags=%d ss=%s" % (w, vpt, B, L, D, fused,
-                                                                            flags, sl))
+    assert len(cases) == 35, sorted(cases)
+    for (w, vpt, k), (B, L, D, fused, flags, sl) in sorted(cases.items()):
+        log("shape W=%d VPT=%d K=%d via B=%d L=%d D=%d fused=%s flags=%d ss=%s" % (
+            w, vpt, k, B, L, D, fused, flags, sl))
         aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
         gl = (FRAME, 1) if flags & rn.RN_GATE else None
         for rms in (False, True):
-            _check_small(rn, orc, 300 + w * 16 + vpt, fused, rms, gl, aff, sl, B, L, D)
+            _check_small(rn, orc, 300 + w * 16 + vpt + k, fused, rms, gl, aff, sl, B, L, D)
 
 
 def test_hip_graph_capture_and_replay(rn, orc):
