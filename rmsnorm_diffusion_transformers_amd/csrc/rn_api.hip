@@ -150,6 +150,7 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
               int streams, rn_layout ss_layout) {
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
+  const int budget = (!fused && (flags & RN_WEIGHT)) ? rn::kVgprBudgetNormAffine : rn::kVgprBudget;
   auto covers = [&](const rn::Shape& s) { return (int64_t)rn::kWaveSize * s.w * s.vpt >= nvec; };
   if (!fused && (flags & RN_WEIGHT) && R * D >= rn::kMultiRowMinElems) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
@@ -161,12 +162,12 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   for (int i = 0; i < rn::kNumShapes; ++i)
     one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && rn::kShapes[i].k == 1 &&
                                       covers(rn::kShapes[i]) &&
-                                      rn::kShapes[i].vpt * ops <= rn::kVgprBudget);
+                                      rn::kShapes[i].vpt * ops <= budget);
   const int want = preferred_waves(R, D, streams, fused, one_wave_fits);
   if (want != 0) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
-      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || s.vpt * ops <= rn::kVgprBudget))
+      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || s.vpt * ops <= budget))
         return i;
     }
   }
@@ -174,7 +175,7 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
     if (s.k > 1 || s.w == 10 || !covers(s)) continue;
-    if (s.vpt * ops <= rn::kVgprBudget) return i;
+    if (s.vpt * ops <= budget) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
   return fallback;

@@ -84,6 +84,15 @@ constexpr int kNumShapes = sizeof(kShapes) / sizeof(kShapes[0]);
 // once, 4 VGPRs per vector per operand, and about 2 waves per SIMD is enough
 // to saturate HBM with this access pattern.
 constexpr int kVgprBudget = 52;
+// The norm-only op with weight keeps weight and bias live through the
+// epilogue next to the whole row (the fused op's x and gate die after the
+// residual update), so its kernels need more registers per operand vector:
+// 253-292 VGPRs at 5 operands x VPT 10 (one wave per SIMD), against 224 for
+// the fused op with gate.  Its tighter budget moves it to 2 x 5 vectors at
+// D = 4608-5120 and 4 x 5 at D = 8704-10240, measured 21 % and 24-32 %
+// faster at 16384-176400 rows with per-row scale/shift (which keeps it off
+// the multi-row shapes) and no slower on small problems.
+constexpr int kVgprBudgetNormAffine = 48;
 // Spacing of loads / stores, in units of 8 cycles (s_nop 7); the streamed
 // row loads of the fused op with one wave per row, and of the norm-only op
 // with binary32 weight/bias, have their own.

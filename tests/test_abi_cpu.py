@@ -231,6 +231,28 @@ def test_describe_launch(rn):
         rn.describe_launch(1, 3, 20000, 0, False)
 
 
+def test_describe_launch_norm_affine_budget(rn):
+    """The norm-only op with weight keeps weight and bias live with the whole
+    row, so it gets a tighter register budget (VPT x operands <= 48): with
+    bf16 weight + bias or a binary32 weight (5 operand vectors per VPT) it
+    leaves one wave x 10 vectors for two x 5 at D 4608-5120 and two x 10 for
+    four x 5 at D 8704-10240; the fused op keeps its shapes."""
+    ROW = (rn.RN_ROW, 0)
+    WB = rn.RN_WEIGHT | rn.RN_BIAS
+    def plan(D, flags, fused=False, adt=rn.RN_DTYPE_BF16, sl=ROW):
+        i = rn.describe_launch(1, 176400, D, flags, fused, (rn.RN_BCAST, 0), sl, affine_dtype=adt)
+        return i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"]
+    assert plan(5120, WB) == (2, 5, 1)
+    assert plan(5120, rn.RN_WEIGHT, adt=rn.RN_DTYPE_F32) == (2, 5, 1)
+    assert plan(4096, WB) == (1, 8, 1)                     # 5 x 8 = 40: one wave still fits
+    assert plan(10240, WB) == (4, 5, 1)
+    assert plan(10240, rn.RN_WEIGHT, adt=rn.RN_DTYPE_F32) == (4, 5, 1)
+    assert plan(5120, rn.RN_WEIGHT) == (1, 10, 1)         # 4 operand vectors: 40
+    assert plan(5120, 0) == (1, 10, 1)
+    # fused, broadcast scale/shift: 5 x 10 = 50 <= 52
+    assert plan(5120, rn.RN_WEIGHT, fused=True, sl=(rn.RN_BCAST, 0)) == (1, 10, 1)
+
+
 def test_describe_launch_multi_row(rn):
     """The norm-only op with weight from 12 Mi elements: one wave streams 4
     consecutive rows through weight, bias, scale and shift loaded once, on
