@@ -151,7 +151,14 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   const int64_t nvec = D / 8;
   const int ops = row_operands(flags, fused, affine_dtype);
   const int budget = (!fused && (flags & RN_WEIGHT)) ? rn::kVgprBudgetNormAffine : rn::kVgprBudget;
+  // the fused op's one-row shapes with one wave per row stage weight and
+  // bias in LDS, so only the row operands take registers
+  const int row_ops = row_operands(flags & ~(uint32_t)(RN_WEIGHT | RN_BIAS), fused, affine_dtype);
   auto covers = [&](const rn::Shape& s) { return (int64_t)rn::kWaveSize * s.w * s.vpt >= nvec; };
+  auto fits = [&](const rn::Shape& s) {
+    if (fused && s.w == 1 && s.k == 1) return s.vpt * row_ops <= budget;
+    return s.vpt * ops <= budget;
+  };
   if (!fused && (flags & RN_WEIGHT) && R * D >= rn::kMultiRowMinElems) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
@@ -161,13 +168,12 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   bool one_wave_fits = false;
   for (int i = 0; i < rn::kNumShapes; ++i)
     one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && rn::kShapes[i].k == 1 &&
-                                      covers(rn::kShapes[i]) &&
-                                      rn::kShapes[i].vpt * ops <= budget);
+                                      covers(rn::kShapes[i]) && fits(rn::kShapes[i]));
   const int want = preferred_waves(R, D, streams, fused, one_wave_fits);
   if (want != 0) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
-      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || s.vpt * ops <= budget))
+      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || fits(s)))
         return i;
     }
   }
@@ -175,7 +181,7 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
     if (s.k > 1 || s.w == 10 || !covers(s)) continue;
-    if (s.vpt * ops <= budget) return i;
+    if (fits(s)) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
   return fallback;

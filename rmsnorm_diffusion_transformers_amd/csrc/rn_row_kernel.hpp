@@ -36,6 +36,12 @@
 //     broadcast and per-frame rows stay resident in L2.
 //   * The row stays in VGPRs (bf16-packed) between the statistics and the
 //     epilogue, so HBM sees each byte once.
+//   * The fused op with one wave per row stages weight and bias in LDS: the
+//     workgroup's waves fill it with buffer loads that write LDS directly
+//     (no registers), issued before the rows' loads, and the epilogue reads
+//     each vector's weight and bias back with ds_read_b128 (LDS reads wait on
+//     lgkmcnt, not on the stores' vmcnt).  The registers then hold only the
+//     row operands, so the fused affine op keeps one wave per row.
 //   * Statistics in fp32.  LayerNorm: the mean, then the centred sum of squares
 //     over the register-resident row.  RMSNorm: the sum of squares.  Wave
 //     reductions are DPP (xor 1, xor 2, half-row mirror, row mirror) then the
@@ -243,6 +249,36 @@ struct AffineRow {
   }
 };
 
+// Weight (and bias) of a one-wave-per-row workgroup, staged in LDS by its
+// RPB waves with buffer loads that write LDS directly.  LDS block (o, v, q)
+// (1 KB: one 16-byte entry per lane) holds, for lane l, the 16-byte half q
+// of operand o's vector v of that lane -- global chunk F * (v * 64 + l) + q
+// -- so the epilogue's reads are contiguous across the wave.  Chunks past
+// the end of a ragged row read as zeros.
+template <class OP, int VPT, int RPB>
+__device__ __forceinline__ void fill_affine_lds(const RowArgs& a, u32x4* lds, uint32_t wave,
+                                                uint32_t lane) {
+  constexpr int F = OP::aff32 ? 2 : 1;
+  constexpr int NBLK = (OP::has_b ? 2 : 1) * VPT * F;
+  const uint32_t abytes = a.d * (OP::aff32 ? 4u : 2u);
+  const auto rw = row_rsrc(a.weight, abytes);
+  const auto rb = row_rsrc(OP::has_b ? a.bias : a.weight, abytes);
+#pragma unroll
+  for (int i = 0; i < (NBLK + RPB - 1) / RPB; ++i) {
+    const uint32_t blk = wave + (uint32_t)(i * RPB);
+    if (blk < (uint32_t)NBLK) {
+      const uint32_t o = blk / (VPT * F);
+      const uint32_t rem = blk - o * (VPT * F);
+      const uint32_t vi = rem / F;
+      const uint32_t q = rem - vi * F;
+      const uint32_t off = (F * (vi * kWaveSize + lane) + q) * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          o ? rb : rw, (__attribute__((address_space(3))) void*)&lds[blk * kWaveSize], 16, off, 0, 0,
+          kPolicyDefault);
+    }
+  }
+}
+
 // Position of one activation row: its index (0 past the last row), its byte
 // offset, and the byte range of its buffers (0 past the last row, which
 // turns every access into a no-op).
@@ -260,6 +296,13 @@ void row_kernel(const RowArgs a) {
   constexpr int VPT = kShapes[SHAPE].vpt;
   constexpr int RPB = kShapes[SHAPE].rpb;
   constexpr int K = kShapes[SHAPE].k;
+  // weight / bias staged in LDS: the fused op, one wave per row, one row per
+  // slot (measured 0.7-7.6 % faster than its previous shapes at D = 2048 to
+  // 5120; the norm-only op, with fewer row operands, ran 2-5 % slower so)
+  constexpr bool kLds = OP::fused && OP::has_w && W == 1 && K == 1;
+  constexpr int F = OP::aff32 ? 2 : 1;
+  constexpr int NBLK = (OP::has_b ? 2 : 1) * VPT * F;
+  [[maybe_unused]] __shared__ u32x4 aff_lds[kLds ? NBLK * kWaveSize : 1];
   constexpr int PL = kPaceLoads;
   constexpr int PS = OP::out == kOutF32 ? kPaceStoresF32 : kPaceStores;
   static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
@@ -285,7 +328,8 @@ void row_kernel(const RowArgs a) {
     p.off = (uint64_t)p.r * (a.d * 2u);
     return p;
   };
-  if constexpr (W == 1) {
+  // (a workgroup that stages weight/bias in LDS keeps every wave to the barrier)
+  if constexpr (W == 1 && !kLds) {
     if (first >= a.rows) return;
   }
   const RowPos p0 = at(first);
@@ -494,14 +538,34 @@ void row_kernel(const RowArgs a) {
       if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
     }
 
+    // weight / bias of vector v: from registers, or (staged in LDS) read into
+    // wl / bl by read_lds(v) before the vector's outputs are computed
+    [[maybe_unused]] AffineRow<OP::aff32, 1> wl, bl;
+    auto read_lds = [&](int v) {
+      if constexpr (kLds) {
+#pragma unroll
+        for (int q = 0; q < F; ++q) {
+          wl.v[0][q] = aff_lds[(v * F + q) * kWaveSize + lane];
+          if constexpr (OP::has_b) bl.v[0][q] = aff_lds[((VPT + v) * F + q) * kWaveSize + lane];
+        }
+      }
+    };
+    auto wval = [&](int v, int j, int k) -> float {
+      if constexpr (kLds) return k ? wl.hi(0, j) : wl.lo(0, j);
+      else return k ? wv.hi(v, j) : wv.lo(v, j);
+    };
+    auto bval = [&](int v, int j, int k) -> float {
+      if constexpr (kLds) return k ? bl.hi(0, j) : bl.lo(0, j);
+      else return k ? bv.hi(v, j) : bv.lo(v, j);
+    };
     // t for element 2j (k = 0) or 2j+1 (k = 1) of vector v
     auto tval = [&](int v, int j, int k) -> float {
       const float hv = k ? hi_f32(h[v][j]) : lo_f32(h[v][j]);
       float n = (hv - mean) * rstd;
       if constexpr (OP::has_w && OP::has_b) {
-        n = __builtin_fmaf(n, k ? wv.hi(v, j) : wv.lo(v, j), k ? bv.hi(v, j) : bv.lo(v, j));
+        n = __builtin_fmaf(n, wval(v, j, k), bval(v, j, k));
       } else if constexpr (OP::has_w) {
-        n *= k ? wv.hi(v, j) : wv.lo(v, j);
+        n *= wval(v, j, k);
       }
       const float s = k ? hi_f32(sc[v][j]) : lo_f32(sc[v][j]);
       const float t = k ? hi_f32(sh[v][j]) : lo_f32(sh[v][j]);
@@ -514,6 +578,7 @@ void row_kernel(const RowArgs a) {
         const auto rs_y = row_rsrc((const char*)a.y + p.off, p.bytes);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
+          read_lds(v);
           u32x4 o;
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] = pack_bf16(tval(v, j, 0), tval(v, j, 1));
@@ -526,6 +591,7 @@ void row_kernel(const RowArgs a) {
         const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)p.r * (a.d * 4u), p.live ? a.d * 4u : 0u);
 #pragma unroll
         for (int v = 0; v < VPT; ++v) {
+          read_lds(v);
           u32x4 o0, o1;
 #pragma unroll
           for (int j = 0; j < 2; ++j) {
@@ -546,6 +612,7 @@ void row_kernel(const RowArgs a) {
       float amax = 0.f;
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
+        read_lds(v);
         float m = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -558,6 +625,7 @@ void row_kernel(const RowArgs a) {
       const auto rs_y = row_rsrc((const char*)a.y + (uint64_t)p.r * a.d, p.live ? a.d : 0u);
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
+        read_lds(v);
         uint32_t w0 = 0, w1 = 0;
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 0, 0) * inv, tval(v, 0, 1) * inv, w0, false);
         w0 = __builtin_amdgcn_cvt_pk_fp8_f32(tval(v, 1, 0) * inv, tval(v, 1, 1) * inv, w0, true);
@@ -579,7 +647,12 @@ void row_kernel(const RowArgs a) {
     // Not with several waves per row: there it delays the row's other waves
     // at the barriers (-12 % measured with binary32 weight/bias).
     if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
-    if constexpr (W == 10) {
+    if constexpr (kLds) {
+      fill_affine_lds<OP, VPT, RPB>(a, aff_lds, wave, lane);
+      load_gate();
+      load_ss_any();
+      load_rows(p0);
+    } else if constexpr (W == 10) {
       load_rows(p0);
       load_gate();
       load_affine();
@@ -595,6 +668,9 @@ void row_kernel(const RowArgs a) {
       load_rows(p0);
     }
     if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
+    // the LDS fill complete in every wave (the compiler waits for the loads
+    // first; no store has been issued yet, so only loads are waited for)
+    if constexpr (kLds) __syncthreads();
     process(p0);
   } else {
     // K consecutive rows share the slot's modulation rows and the affine

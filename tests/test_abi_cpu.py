@@ -207,18 +207,22 @@ def test_describe_launch(rn):
     assert fplan(512, 5120) == (4, 3) and fplan(513, 5120) == (1, 10)
     assert fplan(1024, 5120) == (1, 10) and fplan(1025, 5120) == (2, 5)
     assert fplan(768, 6144) == (4, 3)
-    # binary32 weight/bias count twice against the register budget
+    # the fused op with one wave per row keeps weight/bias in LDS, so only its
+    # 5 row operands count: one wave per row up to D = 5120 for every affine
+    # type; with two or more waves per row weight/bias take registers
+    # (binary32 counting twice)
     wb = rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS
-    a16 = rn.describe_launch(1, 176400, 5120, wb, True)
-    a32 = rn.describe_launch(1, 176400, 5120, wb, True, affine_dtype=rn.RN_DTYPE_F32)
-    assert (a16["waves_per_row"], a16["vec_per_lane"]) == (2, 5)
-    assert (a32["waves_per_row"], a32["vec_per_lane"]) == (2, 5)
-    # fused + gate + weight + bias at D = 3072: 7 (bf16) or 9 (binary32)
-    # operand vectors per VPT; one wave per row needs VPT 6
-    f16 = rn.describe_launch(1, 176400, 3072, wb, True)
-    f32 = rn.describe_launch(1, 176400, 3072, wb, True, affine_dtype=rn.RN_DTYPE_F32)
-    assert (f16["waves_per_row"], f16["vec_per_lane"]) == (1, 6)
-    assert (f32["waves_per_row"], f32["vec_per_lane"]) == (2, 3)
+    for D, want in ((5120, (1, 10)), (3072, (1, 6)), (2048, (1, 4))):
+        for adt in (rn.RN_DTYPE_BF16, rn.RN_DTYPE_F32):
+            i = rn.describe_launch(1, 176400, D, wb, True, affine_dtype=adt)
+            assert (i["waves_per_row"], i["vec_per_lane"]) == want, (D, adt)
+    a32 = rn.describe_launch(1, 110250, 8192, wb, True, affine_dtype=rn.RN_DTYPE_F32)
+    assert (a32["waves_per_row"], a32["vec_per_lane"]) == (4, 4)     # 9 x 8 > 52 at W = 2
+    a16 = rn.describe_launch(1, 110250, 8192, wb, True)
+    assert (a16["waves_per_row"], a16["vec_per_lane"]) == (4, 4)     # 7 x 8 > 52 at W = 2
+    # and from 513 to 1024 rows (the fused op's one-wave band)
+    assert rn.describe_launch(1, 1024, 5120, wb, True,
+                              affine_dtype=rn.RN_DTYPE_F32)["waves_per_row"] == 1
     with pytest.raises(rn.RnError):
         rn.describe_launch(1, 16, 5120, 0, False, affine_dtype=7)
     assert rn.describe_launch(2, 5, 8, 0, False)["grid_blocks"] == 3

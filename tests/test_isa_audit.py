@@ -15,7 +15,10 @@ assembly hipcc writes for them:
     sum each for the mean and for the variance;
   * the instruction counts per row match the design: 10 vectors per lane of
     each of x, residual, gate, and scale/shift (twice: the per-row and the
-    shared-row paths), 20 stores, 80 bf16 packs.
+    shared-row paths), 20 stores, 80 bf16 packs;
+  * the fused op with weight and one wave per row stages weight and bias in
+    LDS with buffer loads that write LDS directly, reads them back with
+    128-bit LDS reads, and keeps the headline kernel's register count.
 """
 import os
 import re
@@ -106,3 +109,24 @@ def test_fp8_kernel_stores(tmp_path):
     assert _count(body, "global_store_dword") == 1       # the per-row scale
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
     assert not re.search(r"^\s+(flat|scratch)_", body, re.M)
+
+
+@pytest.mark.parametrize("aff,lds_loads,lds_reads,lds_bytes", [
+    (4, 10, 40, 40960),    # binary32 weight + bias: 40 1-KB blocks over 4 waves
+    (2, 5, 20, 20480),     # bf16 weight + bias
+    (1, 3, 10, 10240),     # bf16 weight: 10 blocks, 3 rounds over 4 waves
+])
+def test_fused_affine_stages_weight_in_lds(fused_asm, aff, lds_loads, lds_reads, lds_bytes):
+    sym = "_ZN2rn10row_kernelINS_2OpILb0ELb1ELb1ELi%dELi0EEELi7EEEvNS_7RowArgsE" % aff
+    body, meta = _kernel(fused_asm, sym)
+    fills = re.findall(r"^\s+buffer_load_dwordx4 .*\blds\b", body, re.M)
+    assert len(fills) == lds_loads
+    # the row's own loads are those of the headline kernel
+    assert _count(body, "buffer_load_dwordx4") - len(fills) == 70
+    assert _count(body, "ds_read_b128") == lds_reads
+    assert not re.search(r"^\s+ds_(?!read_b128)", body, re.M)   # nothing else touches LDS
+    assert _count(body, "s_barrier") == 1
+    assert _count(body, "buffer_store_dwordx4") == 20
+    assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == lds_bytes
+    assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
+    assert _meta_int(meta, "vgpr_count") <= 256 and not _meta_int(meta, "agpr_count")

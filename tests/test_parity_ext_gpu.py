@@ -212,6 +212,36 @@ def _random_cases(n, seed):
     return cases
 
 
+# The fused op with weight and one wave per row stages weight and bias in
+# LDS: every affine type and output type, 1023 rows (the last workgroup of
+# four rows has one empty slot, whose wave still takes part in the LDS fill
+# and the barrier), ragged and full rows, broadcast and per-frame layouts.
+# (L, D, aff, y dtype, rms, gate layout, scale/shift layout)
+LDS_AFFINE = [
+    (1023, 5120, 1, 0, False, (BCAST, 0), (BCAST, 0)),
+    (1023, 5120, 2, 1, True, (FRAME, 3), (FRAME, 3)),
+    (1023, 5120, 3, 2, False, (BCAST, 0), (FRAME, 3)),
+    (1023, 5120, 4, 0, False, (FRAME, 3), (BCAST, 0)),
+    (1023, 5120, 4, 1, True, (BCAST, 0), (BCAST, 0)),
+    (1023, 5120, 4, 2, True, (BCAST, 0), (FRAME, 3)),
+    (1023, 3000, 4, 0, True, (BCAST, 0), (BCAST, 0)),
+    (1023, 3000, 2, 2, False, (FRAME, 3), (BCAST, 0)),
+    (1023, 1000, 3, 1, False, (BCAST, 0), (FRAME, 3)),
+    (1023, 1000, 1, 0, True, None, (BCAST, 0)),
+]
+
+
+@pytest.mark.parametrize("case", LDS_AFFINE)
+def test_fused_affine_lds(rn, orc, case):
+    L, D, aff, y_dtype, rms, gl, sl = case
+    flags = rn.RN_WEIGHT | (rn.RN_BIAS if aff in (2, 4) else 0) | (rn.RN_GATE if gl else 0)
+    info = rn.describe_launch(1, L, D, flags, True, gl or (BCAST, 0), sl,
+                              affine_dtype=rn.RN_DTYPE_F32 if aff in (3, 4) else rn.RN_DTYPE_BF16)
+    assert (info["waves_per_row"], info["rows_per_wave"]) == (1, 1)
+    log("fused affine, weight/bias in LDS: L=%d D=%d aff=%d y=%d rms=%s gate=%s ss=%s" % case)
+    _run(rn, orc, 1900 + D + 7 * aff + y_dtype, True, rms, gl, aff, sl, 1, L, D, y_dtype)
+
+
 # Multi-row shapes (the norm-only op with weight on large problems): odd row
 # counts (a partly empty last workgroup), ragged rows, every W, affine and
 # output type, broadcast, per-frame (164 tokens per frame) and per-batch
