@@ -27,7 +27,9 @@
 //     per row) at raised wave priority.  Loads and stores share the in-order
 //     vmcnt counter on gfx9, so a load issued after a store could only be
 //     waited for together with that store; issuing every load first keeps the
-//     store latency off the critical path.
+//     store latency off the critical path.  (On the multi-row shapes the
+//     shared rows are loaded once, before the first row, and each further
+//     row's own loads follow the previous row's stores.)
 //   * Loads are issued PL x 8 cycles apart and stores PS x 8 cycles apart
 //     (s_nop): measured on MI355X, back-to-back bursts of 128-bit stores from
 //     every wave stream several percent slower than lightly spaced ones.

@@ -1,0 +1,59 @@
+"""bench.py's host-side helpers (no GPU): the kernel-source digest that ties
+the committed rocprof counter summary to the code it was measured on, and
+the lookup of that summary."""
+import os
+import shutil
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def _copy_sources(tmp_path):
+    for p in bench.KERNEL_SOURCES:
+        dst = tmp_path / p
+        dst.parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(ROOT, p), dst)
+
+
+def _digest_at(monkeypatch, root):
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    return bench.kernel_digest()
+
+
+def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    _copy_sources(tmp_path)
+    base = _digest_at(monkeypatch, tmp_path)
+    kernel = tmp_path / bench.KERNEL_SOURCES[0]
+    text = kernel.read_text()
+    # comments and blank lines only: same digest
+    kernel.write_text("// a new comment line\n\n" + text.replace("// Position of one activation row",
+                                                                  "/* moved */ // Position of an activation row"))
+    assert _digest_at(monkeypatch, tmp_path) == base
+    # a code change: new digest
+    kernel.write_text(text.replace("constexpr int kPolicyStream = 2;", "constexpr int kPolicyStream = 3;"))
+    assert "constexpr int kPolicyStream = 2;" in text
+    assert _digest_at(monkeypatch, tmp_path) != base
+    # so does a change in the shape table header
+    kernel.write_text(text)
+    args = tmp_path / bench.KERNEL_SOURCES[1]
+    args.write_text(args.read_text().replace("constexpr int kPaceStores = 2;", "constexpr int kPaceStores = 3;"))
+    assert _digest_at(monkeypatch, tmp_path) != base
+
+
+def test_committed_traffic_matches_current_sources():
+    """The committed counter summary was taken on the current kernel code, and
+    its HBM bytes are within 0.5 % of the algorithmic bytes."""
+    for wl in ("fused_ln_frame_b1_f49_l176400_d5120", "nss_ln_b1_l176400_d5120"):
+        t = bench.measured_traffic(wl)
+        assert t is not None, wl
+    with open(bench.TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("workload "):
+                tok = line.split()
+                kv = dict(zip(tok[::2], tok[1::2]))
+                assert kv["kernel_digest"] == bench.kernel_digest()
+                hbm, alg = int(kv["hbm_bytes_per_launch"]), int(kv["algorithmic_bytes"])
+                assert abs(hbm / alg - 1) < 0.005, line
