@@ -120,6 +120,16 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
   return n;
 }
 
+// Rows a multiple of 8 KB apart (D % 4096 == 0): shapes whose waves each
+// stream a long exact-cover span of such rows run in one of two modes from
+// one process to the next on MI355X (the fused op at D = 4096 with one wave
+// x 8 vectors: 1.20-1.28 ms in some processes, 1.38-1.42 ms in others, the
+// same code and addresses), which rotating each row's vector order did not
+// remove.  Two waves x 4 vectors measured faster in both modes (1.24 / 1.31
+// ms without affine, 1.25 / 1.27 ms with binary32 weight/bias), so the
+// fused op there takes at least this many waves per row.
+constexpr int kFusedPow2MinWaves = 2;
+
 // Whether every aligned group of k consecutive rows (rows k*m .. k*m + k - 1)
 // shares one scale/shift row: always for a broadcast row, for per-frame rows
 // when the frame length is a multiple of k (frames tile each batch, so the
@@ -159,6 +169,11 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
     if (fused && s.w == 1 && s.k == 1) return s.vpt * row_ops <= budget;
     return s.vpt * ops <= budget;
   };
+  // The fused op with rows a multiple of 8 KB apart (D % 4096 == 0) avoids
+  // one wave per row (see kFusedPow2MinWaves).
+  auto allowed = [&](const rn::Shape& s) {
+    return !(fused && D % 4096 == 0 && s.w < kFusedPow2MinWaves);
+  };
   if (!fused && (flags & RN_WEIGHT) && R * D >= rn::kMultiRowMinElems) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
@@ -168,19 +183,20 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   bool one_wave_fits = false;
   for (int i = 0; i < rn::kNumShapes; ++i)
     one_wave_fits = one_wave_fits || (rn::kShapes[i].w == 1 && rn::kShapes[i].k == 1 &&
-                                      covers(rn::kShapes[i]) && fits(rn::kShapes[i]));
+                                      allowed(rn::kShapes[i]) && covers(rn::kShapes[i]) &&
+                                      fits(rn::kShapes[i]));
   const int want = preferred_waves(R, D, streams, fused, one_wave_fits);
   if (want != 0) {
     for (int i = 0; i < rn::kNumShapes; ++i) {
       const rn::Shape s = rn::kShapes[i];
-      if (s.k == 1 && s.w == want && covers(s) && (want == 10 || fits(s)))
+      if (s.k == 1 && s.w == want && allowed(s) && covers(s) && (want == 10 || fits(s)))
         return i;
     }
   }
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
-    if (s.k > 1 || s.w == 10 || !covers(s)) continue;
+    if (s.k > 1 || s.w == 10 || !allowed(s) || !covers(s)) continue;
     if (fits(s)) return i;
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }

@@ -257,6 +257,26 @@ def test_describe_launch_norm_affine_budget(rn):
     assert plan(5120, rn.RN_WEIGHT, fused=True, sl=(rn.RN_BCAST, 0)) == (1, 10, 1)
 
 
+def test_describe_launch_pow2_fused(rn):
+    """The fused op with rows a multiple of 8 KB apart (D % 4096 == 0) takes
+    at least two waves per row (two waves x 4 vectors at D = 4096, with or
+    without affine); the norm-only op and other widths are unchanged."""
+    def plan(R, D, flags, fused, adt=rn.RN_DTYPE_BF16):
+        i = rn.describe_launch(1, R, D, flags, fused, affine_dtype=adt)
+        return i["waves_per_row"], i["vec_per_lane"]
+    G, WB = rn.RN_GATE, rn.RN_WEIGHT | rn.RN_BIAS
+    assert plan(220500, 4096, G, True) == (2, 4)
+    assert plan(220500, 4096, G | WB, True, rn.RN_DTYPE_F32) == (2, 4)
+    assert plan(220500, 4096, 0, True) == (2, 4)
+    assert plan(800, 4096, G, True) == (2, 4)            # the one-wave band too
+    assert plan(220500, 4096, 0, False) == (1, 8)        # norm-only: unchanged
+    assert plan(441000, 2048, G, True) == (1, 4)         # 4 KB rows: one wave
+    assert plan(176400, 5120, G, True) == (1, 10)        # the headline
+    for D in range(4096, 16385, 4096):
+        for R in (64, 700, 3000, 100000):
+            assert plan(R, D, G, True)[0] >= 2, (R, D)
+
+
 def test_describe_launch_multi_row(rn):
     """The norm-only op with weight from 12 Mi elements: one wave streams 4
     consecutive rows through weight, bias, scale and shift loaded once, on

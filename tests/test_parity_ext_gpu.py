@@ -212,6 +212,30 @@ def _random_cases(n, seed):
     return cases
 
 
+# Power-of-two row widths (D = 4096, 8192, 16384, where every shape covers
+# the row exactly): odd row counts (the last workgroup partly empty), one
+# wave per row with weight and bias in LDS, the multi-row norm-only shapes,
+# several waves per row, every output type.
+# (B, L, D, fused, aff, y dtype, rms, gate layout, scale/shift layout)
+POW2 = [
+    (1, 1023, 4096, True, 0, 0, False, (BCAST, 0), (BCAST, 0)),
+    (1, 1023, 4096, True, 4, 2, True, (FRAME, 3), (FRAME, 3)),
+    (1, 3073, 4096, False, 2, 1, False, None, (BCAST, 0)),     # 4 rows per wave
+    (1, 1025, 8192, True, 3, 0, True, (BCAST, 0), (BCAST, 0)),
+    (2, 1028, 8192, False, 4, 2, False, None, (FRAME, 257)),    # 4 rows per wave, per frame
+    (1, 513, 16384, True, 0, 1, False, (ROW, 0), (BCAST, 0)),
+    (1, 771, 16384, False, 0, 0, True, None, (ROW, 0)),
+    (3, 5, 4096, True, 2, 0, False, (BCAST, 0), (ROW, 0)),
+]
+
+
+@pytest.mark.parametrize("case", POW2)
+def test_power_of_two_widths(rn, orc, case):
+    B, L, D, fused, aff, y_dtype, rms, gl, sl = case
+    log("power-of-two width: B=%d L=%d D=%d fused=%s aff=%d y=%d rms=%s gate=%s ss=%s" % case)
+    _run(rn, orc, 2100 + D // 512 + aff + y_dtype, fused, rms, gl, aff, sl, B, L, D, y_dtype)
+
+
 # The fused op with weight and one wave per row stages weight and bias in
 # LDS: every affine type and output type, 1023 rows (the last workgroup of
 # four rows has one empty slot, whose wave still takes part in the LDS fill
