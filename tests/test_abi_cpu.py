@@ -318,6 +318,46 @@ def test_describe_launch_multi_row(rn):
         assert i["rows_per_block"] == 4 * i["waves_per_block"] // i["waves_per_row"]
 
 
+def test_multi_row_groups_share_modulation_rows(rn):
+    """Whenever the planner gives a problem four rows per wave, every aligned
+    group of four rows maps to one scale/shift row (the index each row takes
+    from its layout: broadcast 0, per row r, per frame b * F + l // (L / F));
+    and a norm-only problem with weight of at least 12 Mi elements whose width
+    a multi-row shape covers gets one whenever its groups share their rows --
+    except per-frame layouts whose frame length is not a multiple of 4, which
+    the planner refuses from the layout alone (their groups can still share
+    rows by chance, e.g. with one batch)."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    BC, ROW, FR = rn.RN_BCAST, rn.RN_ROW, rn.RN_FRAME
+    checked = 0
+    for _ in range(400):
+        B = int(rng.integers(1, 5))
+        F = int(rng.choice([1, 2, 3, 5, 7, 49]))
+        tpf = int(rng.integers(1, 4000))
+        L = F * tpf
+        D = int(rng.integers(1, 1281)) * 8
+        kind = int(rng.integers(0, 3))
+        lay = (kind, F if kind == FR else 0)
+        flags = rn.RN_WEIGHT | (rn.RN_BIAS if rng.random() < 0.5 else 0)
+        if B * L >= 2 ** 31:
+            continue
+        i = rn.describe_launch(B, L, D, flags, False, (BC, 0), lay)
+        R = B * L
+        r = np.arange(R)
+        b, l = r // L, r % L
+        srow = {BC: np.zeros(R, np.int64), ROW: r, FR: b * F + l // tpf}[kind]
+        n = (R // 4) * 4
+        groups_share = bool(np.all(srow[:n].reshape(-1, 4) == srow[:n].reshape(-1, 4)[:, :1])) \
+            and (R % 4 == 0 or bool(np.all(srow[n:] == srow[n])))
+        if i["rows_per_wave"] == 4:
+            assert groups_share, (B, L, D, lay)
+            checked += 1
+        elif R * D >= 12 << 20 and D <= 10240 and kind != ROW:
+            assert not groups_share or kind == FR and tpf % 4 != 0, (B, L, D, lay)
+    assert checked > 50
+
+
 def test_layout_inference(rn):
     import torch
     B, L, D = 2, 12, 16
