@@ -257,6 +257,24 @@ def test_describe_launch_norm_affine_budget(rn):
     assert plan(5120, rn.RN_WEIGHT, fused=True, sl=(rn.RN_BCAST, 0)) == (1, 10, 1)
 
 
+def test_describe_launch_norm_only_eight_vectors(rn):
+    """Large norm-only problems without affine take 8 vectors per lane where
+    the first fit would be 6 (2 or 4 waves per row); the fused op, the
+    norm-only op with weight and small problems keep their shapes."""
+    def plan(R, D, flags=0, fused=False):
+        i = rn.describe_launch(1, R, D, flags, fused)
+        return i["waves_per_row"], i["vec_per_lane"]
+    assert plan(147000, 6144) == (2, 8)
+    assert plan(160000, 5632) == (2, 8)
+    assert plan(73500, 12288) == (4, 8)
+    assert plan(80000, 10752) == (4, 8)
+    assert plan(147000, 6144, rn.RN_GATE, True) == (2, 6)
+    i = rn.describe_launch(1, 147000, 6144, rn.RN_WEIGHT, False, (rn.RN_BCAST, 0), (rn.RN_ROW, 0))
+    assert (i["waves_per_row"], i["vec_per_lane"]) == (2, 6)   # with weight (per-row scale/shift)
+    assert plan(512, 6144) != (2, 8)
+    assert plan(176400, 5120) == (1, 10)
+
+
 def test_describe_launch_pow2_fused(rn):
     """The fused op with rows a multiple of 8 KB apart (D % 4096 == 0) takes
     at least two waves per row (two waves x 4 vectors at D = 4096, with or
