@@ -130,3 +130,25 @@ def test_fused_affine_stages_weight_in_lds(fused_asm, aff, lds_loads, lds_reads,
     assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == lds_bytes
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
     assert _meta_int(meta, "vgpr_count") <= 256 and not _meta_int(meta, "agpr_count")
+
+
+@pytest.fixture(scope="module")
+def nss_asm(tmp_path_factory):
+    return _asm("rn_inst_nss_ln_bf16.hip", tmp_path_factory.mktemp("asm_nss"))
+
+
+@pytest.mark.parametrize("shape,w,vpt", [(31, 2, 5), (27, 1, 4)])
+def test_multi_row_kernel_loads_shared_rows_once(nss_asm, shape, w, vpt):
+    """The norm-only op with binary32 weight + bias on a multi-row shape (4
+    consecutive rows per wave): the x loads and the stores of 4 rows, the
+    weight, bias, scale and shift loads once (scale/shift on both cache-policy
+    paths), 4 rows of bf16 packs; barriers only with several waves per row."""
+    sym = "_ZN2rn10row_kernelINS_2OpILb0ELb0ELb0ELi4ELi0EEELi%dEEEvNS_7RowArgsE" % shape
+    body, meta = _kernel(nss_asm, sym)
+    k = 4
+    assert _count(body, "buffer_load_dwordx4") == k * vpt + 2 * 2 * vpt + 2 * 2 * vpt
+    assert _count(body, "buffer_store_dwordx4") == k * vpt
+    assert _count(body, "v_cvt_pk_bf16_f32") == k * vpt * 4
+    assert (_count(body, "s_barrier") > 0) == (w > 1)
+    assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
+    assert _meta_int(meta, "vgpr_count") <= 256 and not _meta_int(meta, "agpr_count")
