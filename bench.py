@@ -8,10 +8,12 @@ PR #36349, "Microbenchmark", with synthetic N(0,1) activations.  Inputs are
 resident in HBM before the timed region.
 
 Metric: algorithmic HBM bytes (every operand read once + every output written
-once) / time, in GB/s (1e9 B/s), against the 8 TB/s HBM3E peak.  The
-norm-only companion (same shape, broadcast scale/shift) is reported beside it.
+once) / time, in GB/s (1e9 B/s), against the 8 TB/s HBM3E peak.
 
-Beside the headline the line carries: the norm-only companion; variants of
+Beside the headline the line carries: companions (the norm-only op at the
+same shape with broadcast scale/shift, and the other large workloads: fused
+LayerNorm at L 90000 with 1 % of rows scaled by 50, fused RMSNorm + weight
+with per-row scale/shift at L 90000, D 10240); variants of
 the op at the same shape (broadcast modulation with and without binary32
 weight+bias, FP8 and binary32 outputs, per-batch modulation); a DiT-forward
 mix of the three calls WAN2.2 makes per forward (41 norm-only + 40 fused with
@@ -39,7 +41,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 HEADLINE = "fused_ln_frame_b1_f49_l176400_d5120"
-COMPANION = "nss_ln_b1_l176400_d5120"
+# Reported beside the headline: the norm-only op at the same shape, and the
+# other large workloads (fused LayerNorm at L 90000 with 1 % of rows scaled
+# by 50; fused RMSNorm + weight with per-row scale/shift at D 10240).
+COMPANIONS = ["nss_ln_b1_l176400_d5120", "fused_ln_b1_l90000_d5120",
+              "fused_rms_w_b1_l90000_d10240"]
 KERNEL_SOURCES = ["rmsnorm_diffusion_transformers_amd/csrc/rn_row_kernel.hpp",
                   "rmsnorm_diffusion_transformers_amd/csrc/rn_args.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -434,14 +440,18 @@ def main():
                                                           HBM_PEAK_GBS))
     companions = []
     if not args.no_companion and args.workload == HEADLINE:
-        wc = synth.WORKLOADS[COMPANION]
-        cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True)
-        cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
-        log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
-        companions.append({"workload": wc.name, "ms_per_launch": round(cms, 5),
-                           "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes": wc.algorithmic_bytes(),
-                           "traffic": measured_traffic(wc.name), "launch_ms": cstats})
+        for name in COMPANIONS:
+            wc = synth.WORKLOADS[name]
+            cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True)
+            cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
+            log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
+            ci = rn.describe_launch(wc.B, wc.L, wc.D, flags_of(rn, wc), wc.op == "fused",
+                                    wc.gate_layout or (0, 0), wc.ss_layout)
+            companions.append({"workload": wc.name, "ms_per_launch": round(cms, 5),
+                               "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
+                               "algorithmic_bytes": wc.algorithmic_bytes(),
+                               "traffic": measured_traffic(wc.name), "launch_ms": cstats,
+                               "launch": ci})
     info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused",
                               wl.gate_layout or (0, 0), wl.ss_layout)
     ref = copy_reference(args.steps, args.warmup, dev)
