@@ -666,3 +666,69 @@ def test_rescaled_statistics_ext_outputs(rn, orc):
             log("rescaled statistics ext: D=%d L=%d fused=%s aff=%d y=%d W=%d K=%d" % (
                 D, L, fused, aff, y_dtype, info["waves_per_row"], info["rows_per_wave"]))
             _run_inputs(rn, orc, inp, fused, False, gl, aff, (BCAST, 0), 1, L, D, y_dtype)
+
+
+def test_hip_graph_lds_and_multi_row(rn, orc):
+    """The LDS-staged fused kernel (binary32 weight + bias, one wave per row)
+    and a multi-row norm-only kernel (bf16 weight + bias, 4 rows per wave)
+    captured in one HIP graph and replayed three times with new input
+    contents, eager work between replays, each replay against the oracle."""
+    B, D = 1, 5120
+    LA, LB = 600, 2458                        # 2458 x 5120 >= 12 Mi elements
+    WB = rn.RN_WEIGHT | rn.RN_BIAS
+    ia = rn.describe_launch(B, LA, D, rn.RN_GATE | WB, True, affine_dtype=rn.RN_DTYPE_F32)
+    ib = rn.describe_launch(B, LB, D, WB, False)
+    assert (ia["waves_per_row"], ia["rows_per_wave"]) == (1, 1)
+    assert ib["rows_per_wave"] == 4
+
+    def dev_like(a):
+        dt = torch.float32 if a.dtype == np.float32 else torch.bfloat16
+        return torch.empty(a.shape, dtype=dt, device="cuda")
+
+    pa = _problem(1, True, (BCAST, 0), 4, (BCAST, 0), B, LA, D)
+    pb = _problem(2, False, None, 2, (BCAST, 0), B, LB, D)
+    da = {k: dev_like(v) for k, v in pa.items()}
+    db = {k: dev_like(v) for k, v in pb.items()}
+    ya = torch.empty((LA, D), dtype=torch.bfloat16, device="cuda")
+    ra = torch.empty_like(ya)
+    yb = torch.empty((LB, D), dtype=torch.bfloat16, device="cuda")
+
+    def fill(seed):
+        inps = (_problem(seed, True, (BCAST, 0), 4, (BCAST, 0), B, LA, D),
+                _problem(seed + 100, False, None, 2, (BCAST, 0), B, LB, D))
+        for inp, d in zip(inps, (da, db)):
+            for k, v in inp.items():
+                d[k].copy_(f32_dev(v) if v.dtype == np.float32 else to_dev(v))
+        return inps
+
+    def calls():
+        rn.resnorm_fused_fwd_ex(ya, ra, da["x"], da["residual"], da["gate"], da["weight"],
+                                da["bias"], da["scale"], da["shift"], B, LA, D, rn.RN_GATE | WB,
+                                (BCAST, 0), (BCAST, 0), 1e-6, rn.RN_DTYPE_F32)
+        rn.norm_scale_shift_fwd(yb, db["x"], db["weight"], db["bias"], db["scale"], db["shift"],
+                                B, LB, D, WB, (BCAST, 0), 1e-6)
+
+    fill(3)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    for seed in (21, 22, 23):
+        a, b = fill(seed)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log("graph replay %d: LDS-staged fused and multi-row norm-only" % seed)
+        y_ref, ro_ref, _ = orc.fused(a["x"], a["residual"], a["gate"], a["weight"], a["bias"],
+                                     a["scale"], a["shift"], B, LA, D, False, (BCAST, 0), (BCAST, 0),
+                                     1e-6, affine_f32=True, threads=THREADS)
+        compare_outputs(to_host(ya), y_ref, to_host(ra), ro_ref, "graph replay %d fused" % seed)
+        yb_ref, _ = orc.nss(b["x"], b["weight"], b["bias"], b["scale"], b["shift"], B, LB, D, False,
+                            (BCAST, 0), 1e-6, threads=THREADS)
+        compare_outputs(to_host(yb), yb_ref, what="graph replay %d nss" % seed)
+        torch.add(da["x"], 1.0).sum().item()      # eager work between replays
