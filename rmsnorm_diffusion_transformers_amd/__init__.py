@@ -105,23 +105,34 @@ def _check(status: int):
         raise RnError(status, last_error())
 
 
-_DTYPE_NAMES = {RN_DTYPE_BF16: "bfloat16", RN_DTYPE_F32: "float32",
-                RN_DTYPE_FP8_E4M3: "float8_e4m3fn"}
+_torch = None          # torch, imported on first use (the C ABI works without it)
+_TORCH_DTYPES = {}     # RN_DTYPE_* -> torch dtype
+
+
+def _torch_mod():
+    global _torch
+    if _torch is None:
+        import torch
+        _TORCH_DTYPES.update({RN_DTYPE_BF16: torch.bfloat16, RN_DTYPE_F32: torch.float32,
+                              RN_DTYPE_FP8_E4M3: torch.float8_e4m3fn})
+        _torch = torch
+    return _torch
 
 
 def _addr(t, dtype=RN_DTYPE_BF16):
     """Device address of a contiguous CUDA tensor of the given element type
-    (or an int address, or None)."""
+    (or an int address, or None).  Runs on every call, so it sticks to cheap
+    attribute checks."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
-    import torch
+    torch = _torch_mod()
     if not isinstance(t, torch.Tensor):
         raise TypeError("expected a torch.Tensor, an int address or None, got %r" % type(t))
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError("tensor must be on a GPU device (got %s); there is no CPU path" % t.device)
-    want = getattr(torch, _DTYPE_NAMES[dtype])
+    want = _TORCH_DTYPES[dtype]
     if t.dtype != want:
         raise TypeError("tensor must be %s (got %s)" % (want, t.dtype))
     if not t.is_contiguous():
@@ -151,8 +162,7 @@ def _check_tensors(named):
     elements as the sizes and layouts make the kernel touch.  `named` is a
     sequence of (name, tensor or address or None, elements needed).  Returns
     the device index (None when only addresses were given)."""
-    import torch
-    Tensor = torch.Tensor
+    Tensor = _torch_mod().Tensor
     dev = first = None
     for name, t, need in named:
         if not isinstance(t, Tensor):
@@ -171,8 +181,7 @@ def _stream(stream, device=None):
     """The stream to enqueue on: the given one, else torch's current stream of
     the operands' device."""
     if stream is None:
-        import torch
-        return torch.cuda.current_stream(device).cuda_stream
+        return _torch_mod().cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
@@ -311,8 +320,8 @@ def _affine_dtype(weight, bias) -> int:
 
 
 def _new_y(x, y_dtype):
-    import torch
-    return torch.empty(x.shape, dtype=getattr(torch, _DTYPE_NAMES[y_dtype]), device=x.device)
+    torch = _torch_mod()
+    return torch.empty(x.shape, dtype=_TORCH_DTYPES[y_dtype], device=x.device)
 
 
 def fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
