@@ -554,3 +554,40 @@ def test_last_error_is_per_thread(rn):
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_describe_launch_properties(rn):
+    """Seeded random problems over the whole valid input space: every plan
+    covers D, counts enough workgroups for every row, keeps workgroups within
+    1024 threads, and gives several rows per wave only to the norm-only op
+    with weight on problems of at least 12 Mi elements; invalid sizes are
+    refused with an error, never planned."""
+    import numpy as np
+    rng = np.random.default_rng(7)
+    for _ in range(3000):
+        fused = bool(rng.random() < 0.5)
+        flags = int(rng.integers(0, 16))
+        if not fused:
+            flags &= ~rn.RN_GATE
+        if flags & rn.RN_BIAS:
+            flags |= rn.RN_WEIGHT
+        B = int(rng.integers(0, 5))
+        L = int(rng.choice([1, 3, 16, 600, 3600, 90000, 176400]))
+        D = int(rng.integers(1, rn.RN_D_MAX // 8 + 1)) * 8
+        lay = lambda: [(rn.RN_BCAST, 0), (rn.RN_ROW, 0), (rn.RN_FRAME, 1), (rn.RN_FRAME, 3)][int(rng.integers(0, 4))]  # noqa: E731
+        gl, sl = lay(), lay()
+        adt = rn.RN_DTYPE_F32 if rng.random() < 0.5 else rn.RN_DTYPE_BF16
+        i = rn.describe_launch(B, L, D, flags, fused, gl, sl, affine_dtype=adt)
+        R = B * L
+        assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
+        assert i["block_threads"] == 64 * i["waves_per_block"] <= 1024
+        assert i["rows_per_block"] == i["rows_per_wave"] * i["waves_per_block"] // i["waves_per_row"]
+        assert i["grid_blocks"] * i["rows_per_block"] >= R
+        assert i["grid_blocks"] == -(-R // i["rows_per_block"])
+        assert i["rows_per_wave"] in (1, 4)
+        if i["rows_per_wave"] == 4:
+            assert not fused and flags & rn.RN_WEIGHT and R * D >= 12 << 20
+    for bad in ((1, 16, 7, 0), (1, 16, 0, 0), (1, 16, rn.RN_D_MAX + 8, 0), (-1, 16, 64, 0),
+                (1, 16, 64, rn.RN_BIAS), (1, 16, 64, 1 << 7)):
+        with pytest.raises(rn.RnError):
+            rn.describe_launch(*bad, False)
