@@ -193,7 +193,9 @@ typedef struct {
 rn_status rn_describe_launch(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
                              rn_layout gate_layout, rn_layout ss_layout, rn_launch_info* info);
 /* The same for the *_ex entry points' element types (ext may be NULL: all
- * bf16).  RN_EINVAL for an unknown affine_dtype. */
+ * bf16).  RN_EINVAL for an unknown affine_dtype; both forms refuse, with the
+ * launch's status and message, the shapes and layouts a launch would refuse
+ * (pointers are not examined). */
 rn_status rn_describe_launch_ex(int64_t B, int64_t L, int64_t D, uint32_t flags, int32_t fused,
                                 rn_layout gate_layout, rn_layout ss_layout, const rn_ext* ext,
                                 rn_launch_info* info);

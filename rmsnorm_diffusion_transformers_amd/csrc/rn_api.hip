@@ -441,6 +441,9 @@ rn_status rn_describe_launch_ex(int64_t B, int64_t L, int64_t D, uint32_t flags,
   const int affine_dtype = ext ? ext->affine_dtype : RN_DTYPE_BF16;
   if (affine_dtype != RN_DTYPE_BF16 && affine_dtype != RN_DTYPE_F32)
     return fail(RN_EINVAL, "affine_dtype %d is not RN_DTYPE_BF16 or RN_DTYPE_F32", affine_dtype);
+  // the layouts a launch would refuse are refused here too
+  if (fused && (flags & RN_GATE) && (st = check_layout("gate", gate_layout, L)) != RN_OK) return st;
+  if ((st = check_layout("scale/shift", ss_layout, L)) != RN_OK) return st;
   const int vi = shape_for(B * L, L, D, flags, fused != 0, affine_dtype,
                            hbm_streams(flags, fused != 0, gate_layout, ss_layout), ss_layout);
   if (vi < 0) return fail(RN_EUNSUPPORTED, "no compiled shape covers D=%lld", (long long)D);

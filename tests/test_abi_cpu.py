@@ -328,7 +328,10 @@ def test_describe_launch_multi_row(rn):
     assert k_of(2, 8196, 5120, W, sl=frame(1))[2] == 4          # per batch, L % 4 == 0
     assert k_of(2, 8194, 5120, W, sl=frame(1))[2] == 1          # per batch, L % 4 == 2
     assert k_of(1, 176400, 5120, W, sl=(rn.RN_ROW, 0))[2] == 1
-    assert k_of(1, 176400, 5120, W, sl=frame(0))[2] == 1        # invalid layout: no multi-row
+    with pytest.raises(rn.RnError, match="frames >= 1"):
+        k_of(1, 176400, 5120, W, sl=frame(0))                    # refused, as a launch would be
+    with pytest.raises(rn.RnError, match="L % frames == 0"):
+        k_of(1, 176400, 5120, W, sl=frame(17))
     for D in range(8, 10241, 8):
         i = rn.describe_launch(1, -(-(12 << 20) // D), D, WB, False)
         assert i["rows_per_wave"] == 4 and i["vec_per_lane"] <= 5
@@ -577,6 +580,12 @@ def test_describe_launch_properties(rn):
         lay = lambda: [(rn.RN_BCAST, 0), (rn.RN_ROW, 0), (rn.RN_FRAME, 1), (rn.RN_FRAME, 3)][int(rng.integers(0, 4))]  # noqa: E731
         gl, sl = lay(), lay()
         adt = rn.RN_DTYPE_F32 if rng.random() < 0.5 else rn.RN_DTYPE_BF16
+        bad = [lay for lay in ((gl if fused and flags & rn.RN_GATE else None), sl)
+               if lay is not None and lay[0] == rn.RN_FRAME and L % lay[1]]
+        if bad:
+            with pytest.raises(rn.RnError, match="L % frames == 0"):
+                rn.describe_launch(B, L, D, flags, fused, gl, sl, affine_dtype=adt)
+            continue
         i = rn.describe_launch(B, L, D, flags, fused, gl, sl, affine_dtype=adt)
         R = B * L
         assert 64 * i["waves_per_row"] * i["vec_per_lane"] * 8 >= D
