@@ -600,3 +600,23 @@ def test_describe_launch_properties(rn):
                 (1, 16, 64, rn.RN_BIAS), (1, 16, 64, 1 << 7)):
         with pytest.raises(rn.RnError):
             rn.describe_launch(*bad, False)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built HIP library the binding refuses to import (no CPU
+    fallback exists): a copy of the package without librnorm.so raises
+    ImportError naming the missing library and how to build it."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "rmsnorm_diffusion_transformers_amd", "__init__.py")
+    pkg = tmp_path / "rmsnorm_diffusion_transformers_amd"
+    pkg.mkdir()
+    shutil.copy(src, pkg / "__init__.py")
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "try:\n    import rmsnorm_diffusion_transformers_amd\n"
+            "except ImportError as e:\n    print('IMPORTERROR', e)\n"
+            "else:\n    print('IMPORTED')\n") % str(tmp_path)
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert "IMPORTERROR" in out.stdout, out.stdout + out.stderr
+    assert "librnorm.so is not built" in out.stdout and "build()" in out.stdout
