@@ -595,6 +595,25 @@ def pin_fp8_rows(o, seed: int = 15):
     assert s[0] == np.float32(np.abs(t[0][fin]).max() / 448.0) and y[0, 3] == nan_code
 
 
-FAST_PINS = [pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
+def pin_golden_worked_rows(o):
+    """The hand-worked rows of tests/golden/worked_rows.txt: dyadic inputs whose
+    results follow exactly from the definition (residual ties to even, gate 0,
+    1/2 and 2, eps inside the square root, the biased variance, uncentred
+    RMSNorm, affine before modulation, per-frame and per-row operand rows, a
+    constant row).  Every bit of y and residual_out must match."""
+    from golden_cases import load_cases
+    for c in load_cases():
+        common = dict(B=c["B"], L=c["L"], D=c["D"], is_rms=c["norm"] == "rms",
+                      ss_layout=c["layout.ss"], eps=c["eps"])
+        if c["op"] == "fused":
+            y, ro, _ = o.fused(c["x"], c["residual"], c["gate"], c.get("weight"), c.get("bias"),
+                               c["scale"], c["shift"], gate_layout=c["layout.gate"], **common)
+            assert np.array_equal(ro.ravel(), c["expect.residual_out"]), c["name"]
+        else:
+            y, _ = o.nss(c["x"], c.get("weight"), c.get("bias"), c["scale"], c["shift"], **common)
+        assert np.array_equal(y.ravel(), c["expect.y"]), c["name"]
+
+
+FAST_PINS = [pin_golden_worked_rows, pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
              pin_torch_norms, pin_layouts, pin_fused_is_nss_of_residual, pin_scale_invariance,
              pin_random_rows_ld, pin_invariants]
