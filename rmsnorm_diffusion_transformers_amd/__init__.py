@@ -63,6 +63,15 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError("librnorm.so is not built (expected at %s); build it with "
                           "__graft_entry__.build() or python %s/_build.py" % (LIB_PATH, _HERE))
+    # One HIP runtime per process.  torch ships its own copies of the HIP and
+    # HSA runtimes; if this library were mapped first, its libamdhip64.so.7
+    # would pull in the system copies and torch would then add its own, and
+    # with two HSA runtimes in one process one of them can find no device.
+    # Importing torch first makes the library resolve to torch's copy.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P, I64, U32, F32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
     lib.resnorm_fused_fwd.argtypes = [P, P, P, P, P, P, P, P, P, I64, I64, I64, U32,

@@ -620,3 +620,22 @@ def test_missing_library_fails_loudly(tmp_path):
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert "IMPORTERROR" in out.stdout, out.stdout + out.stderr
     assert "librnorm.so is not built" in out.stdout and "build()" in out.stdout
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch must not map a second HIP or HSA
+    runtime next to torch's own copies (two runtimes in one process can leave
+    one of them without a device)."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import rmsnorm_diffusion_transformers_amd\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "libs = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l or 'libhsa-runtime64' in l})\n"
+            "print('\\n'.join(libs))\n") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    libs = out.stdout.split()
+    assert len([l for l in libs if "libamdhip64" in l]) == 1, libs
+    assert len([l for l in libs if "libhsa-runtime64" in l]) == 1, libs
