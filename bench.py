@@ -10,6 +10,14 @@ resident in HBM before the timed region.
 Metric: algorithmic HBM bytes (every operand read once + every output written
 once) / time, in GB/s (1e9 B/s), against the 8 TB/s HBM3E peak.
 
+Placement: by default the streamed tensors (x, residual and any per-row
+operands; y and residual_out) live in one HBM arena at offsets chosen by
+measurement (rmsnorm_diffusion_transformers_amd.hbm: inputs in one 32 GiB
+granule, each output in its own granule of another class).  The rate with
+torch's own back-to-back allocations on the fresh device is measured first
+and reported beside it (placement.default_allocation); --placement default
+times that layout throughout.
+
 Beside the headline the line carries: companions (the norm-only op at the
 same shape with broadcast scale/shift, and the other large workloads: fused
 LayerNorm at L 90000 with 1 % of rows scaled by 50, fused RMSNorm + weight
@@ -22,8 +30,9 @@ affine + 40 fused without, broadcast modulation, as in sglang PR #36349,
 reference; and the CPU oracle baseline.
 
 Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
-GPU), --steps K, --warmup W, --calibrate (time a plain elementwise copy, used to
-scale rocprof byte counters), --no-cpu-baseline, --no-extras, --workload NAME.
+GPU), --steps K, --warmup W, --placement planned|default, --calibrate (time a
+plain elementwise copy, used to scale rocprof byte counters), --no-cpu-baseline,
+--no-extras, --workload NAME.
 """
 from __future__ import annotations
 
@@ -133,37 +142,120 @@ def launch_stats(fn, steps):
             "n": len(ts)}
 
 
-def time_workload(rn, wl, steps, warmup, dev, keep=False, stats=False):
+def streamed_keys(wl):
+    """The inputs with one row per activation row (each read once per launch)."""
+    keys = ["x"]
+    if wl.op == "fused":
+        keys.append("residual")
+        if wl.gate_layout is not None and wl.gate_layout[0] == 1:
+            keys.append("gate")
+    if wl.ss_layout[0] == 1:
+        keys += ["scale", "shift"]
+    return keys
+
+
+def host_bf16(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def plan_workload(rn, wl, inp, arena, dev, extra_out_bytes=()):
+    """Measured placement of the workload's streamed inputs and its outputs in
+    the arena (rmsnorm_diffusion_transformers_amd.hbm.plan); extra outputs
+    share y's granule."""
     import torch
 
-    import synth
+    from rmsnorm_diffusion_transformers_amd import hbm
+    keys = streamed_keys(wl)
+    small = upload({k: v for k, v in inp.items() if k not in keys}, dev)
+    nb = wl.R * wl.D * 2
+    writes = [[nb, *extra_out_bytes] if extra_out_bytes else nb] + ([nb] if wl.op == "fused" else [])
+    stream = torch.cuda.current_stream()
+    shape = inp["x"].shape
 
+    def make_launch(r_off, w_off):
+        d = dict(small)
+        for k, off in zip(keys, r_off):
+            d[k] = arena.view(off, inp[k].shape, torch.bfloat16)
+        y_off = w_off[0][0] if isinstance(w_off[0], list) else w_off[0]
+        y = arena.view(y_off, shape, torch.bfloat16)
+        ro = arena.view(w_off[1], shape, torch.bfloat16) if wl.op == "fused" else None
+        return lambda: launch_workload(rn, wl, d, y, ro, stream)
+
+    t0 = time.time()
+    pl = hbm.plan(arena, [inp[k].nbytes for k in keys], writes, make_launch, stream=stream)
+    info = pl.describe()
+    info["search_s"] = round(time.time() - t0, 2)
+    log("%s: placement inputs @ granule %d, outputs @ %s (%d candidates %.4f..%.4f ms, chosen %.4f ms, "
+        "%.1f s)" % (wl.name, pl.read_granule, list(pl.write_granules), pl.candidates,
+                     info["ms_first_pass_best"], info["ms_first_pass_worst"], pl.ms, info["search_s"]))
+    return pl, info
+
+
+def device_tensors(wl, inp, dev, arena=None, placement=None, extra_out=()):
+    """(operands, y, residual_out, extra outputs) on the device: torch's own
+    allocations, or views of the arena at the planned offsets with the inputs
+    copied in.  extra_out lists (shape, dtype) of outputs placed after y."""
+    import torch
+    fused = wl.op == "fused"
+    if placement is None:
+        d = upload(inp, dev)
+        y = torch.empty_like(d["x"])
+        ro = torch.empty_like(d["x"]) if fused else None
+        extra = [torch.empty(shape, dtype=dt, device=dev) for shape, dt in extra_out]
+        return d, y, ro, extra
+    keys = streamed_keys(wl)
+    d = upload({k: v for k, v in inp.items() if k not in keys}, dev)
+    for k, off in zip(keys, placement.read_offsets):
+        t = arena.view(off, inp[k].shape, torch.bfloat16)
+        t.copy_(host_bf16(inp[k]))
+        d[k] = t
+    w0 = placement.write_offsets[0]
+    y_offs = w0 if isinstance(w0, list) else [w0]
+    y = arena.view(y_offs[0], inp["x"].shape, torch.bfloat16)
+    extra = [arena.view(o, shape, dt) for o, (shape, dt) in zip(y_offs[1:], extra_out)]
+    ro = arena.view(placement.write_offsets[1], inp["x"].shape, torch.bfloat16) if fused else None
+    torch.cuda.synchronize()
+    return d, y, ro, extra
+
+
+def make_inputs(wl):
+    import synth
     t0 = time.time()
     inp = synth.make_inputs(wl, threads=threads())
     log("%s: inputs generated in %.1f s" % (wl.name, time.time() - t0))
-    d = upload(inp, dev)
+    return inp
+
+
+def time_workload(rn, wl, steps, warmup, dev, keep=False, stats=False, inp=None, arena=None,
+                  placement=None, extra_out=()):
+    import torch
+
+    if inp is None:
+        inp = make_inputs(wl)
+    d, y, ro, extra = device_tensors(wl, inp, dev, arena, placement, extra_out)
     del inp
-    y = torch.empty_like(d["x"])
-    ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
     stream = torch.cuda.current_stream()
     call = lambda: launch_workload(rn, wl, d, y, ro, stream)  # noqa: E731
     ms, wall = time_calls(call, steps, warmup)
     per_launch = launch_stats(call, steps) if stats else None
     if keep:
-        return ms, wall, per_launch, (d, y, ro)
-    del d, y, ro
+        return ms, wall, per_launch, (d, y, ro, extra)
+    del d, y, ro, extra
     torch.cuda.empty_cache()
     return ms, wall, per_launch
 
 
 def extras(rn, dev_tensors, steps, warmup):
     """Variants of the op and the DiT-forward mix at the headline shape, on the
-    headline's resident x / residual (B 1, L 176400, D 5120)."""
+    headline's resident x / residual (B 1, L 176400, D 5120) and its outputs
+    (y, residual_out, and the binary32 and FP8 y placed beside y)."""
     import numpy as np
     import torch
 
     import synth
-    d, y, ro = dev_tensors
+    d, y, ro, (y32, y8) = dev_tensors
     x, res = d["x"], d["residual"]
     R, D = x.shape
     dev = x.device
@@ -177,8 +269,6 @@ def extras(rn, dev_tensors, steps, warmup):
     G, W, Bi = rn.RN_GATE, rn.RN_WEIGHT, rn.RN_BIAS
     F32, FP8 = rn.RN_DTYPE_F32, rn.RN_DTYPE_FP8_E4M3
     BC, FR = (rn.RN_BCAST, 0), (rn.RN_FRAME, 49)
-    y32 = torch.empty((R, D), dtype=torch.float32, device=dev)
-    y8 = torch.empty((R, D), dtype=torch.float8_e4m3fn, device=dev)
     ys = torch.empty((R,), dtype=torch.float32, device=dev)
 
     def fused_bcast():
@@ -258,7 +348,7 @@ def extras(rn, dev_tensors, steps, warmup):
                      "fused, no affine": 40},
            "shape": "B 1, L 176400, D 5120, broadcast (1,C) gate/scale/shift, LayerNorm",
            "pages_prior_art_ms_per_forward_context": [171.6, 174.8]}
-    del y32, y8, ys, bc, pb, w32, b32, w16, b16
+    del ys, bc, pb, w32, b32, w16, b16
     return out, mix
 
 
@@ -405,6 +495,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--placement", choices=("planned", "default"), default="planned",
+                    help="planned: streamed tensors in an HBM arena at measured offsets; "
+                         "default: torch's own allocations")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-companion", action="store_true")
@@ -424,34 +517,94 @@ def main():
 
     import rmsnorm_diffusion_transformers_amd as rn
     import synth
+    from rmsnorm_diffusion_transformers_amd import hbm
     wl = synth.WORKLOADS[args.workload]
     want_extras = not args.no_extras and args.workload == HEADLINE
-    if want_extras:
-        ms, wall, per_launch, kept = time_workload(rn, wl, args.steps, args.warmup, dev,
-                                                   keep=True, stats=True)
-        variants, mix = extras(rn, kept, args.steps, args.warmup)
-        del kept
-        torch.cuda.empty_cache()
-    else:
-        ms, wall, per_launch = time_workload(rn, wl, args.steps, args.warmup, dev, stats=True)
+    companions_wanted = not args.no_companion and args.workload == HEADLINE
     nbytes = wl.algorithmic_bytes()
+    inp = make_inputs(wl)
+    extra_out = [((wl.R, wl.D), torch.float32), ((wl.R, wl.D), torch.float8_e4m3fn)] if want_extras else []
+    extra_bytes = [wl.R * wl.D * 4, wl.R * wl.D] if want_extras else []
+
+    # Row-kernel launches before the timed workloads (the default-allocation
+    # pass and the placement trials), so that a kernel trace can be split.
+    prelude = 0
+    placement = {"kind": "default"}
+    arena = None
+    plans = {}
+    comp_inputs = {}
+    if args.placement == "planned":
+        # what torch's own allocations give on a fresh device, measured first
+        dms, _, _ = time_workload(rn, wl, args.steps, args.warmup, dev, inp=inp)
+        prelude += args.steps + args.warmup
+        dg = nbytes / (dms * 1e-3) / 1e9
+        log("%s, torch allocations: %.4f ms/launch, %.1f GB/s" % (wl.name, dms, dg))
+        placement["default_allocation"] = {"ms_per_launch": round(dms, 5), "GB/s": round(dg, 1),
+                                           "frac": round(dg / HBM_PEAK_GBS, 4)}
+        try:
+            arena = hbm.HbmArena(dev)
+        except RuntimeError as e:
+            log("no HBM arena (%s); torch allocations are used" % e)
+            placement["note"] = str(e)
+    if arena is not None:
+        placement["kind"] = "planned"
+        placement["arena_granules"] = arena.granules
+        pl, info = plan_workload(rn, wl, inp, arena, dev, extra_bytes)
+        plans[wl.name] = pl
+        placement.update(info)
+        prelude += hbm.launches(pl.candidates)
+        if companions_wanted:
+            for name in COMPANIONS:
+                wc = synth.WORKLOADS[name]
+                comp_inputs[name] = make_inputs(wc)
+                plans[name], _ = plan_workload(rn, wc, comp_inputs[name], arena, dev)
+                prelude += hbm.launches(plans[name].candidates)
+    log("row-kernel launches before the timed workloads: %d" % prelude)
+
+    pl = plans.get(wl.name)
+    ms, wall, per_launch, kept = time_workload(rn, wl, args.steps, args.warmup, dev, keep=True,
+                                               stats=True, inp=inp, arena=arena, placement=pl,
+                                               extra_out=extra_out)
+    del inp
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("%s: %.4f ms/launch, %.1f GB/s (%.1f%% of %g)" % (wl.name, ms, gbs, 100 * gbs / HBM_PEAK_GBS,
                                                           HBM_PEAK_GBS))
+    copy_placed = None
+    if pl is not None:
+        d, y = kept[0], kept[1]
+        cms, _ = time_calls(lambda: torch.neg(d["x"], out=y), args.steps, args.warmup)
+        nb = 2 * wl.R * wl.D * 2
+        copy_placed = {"kernel": "torch.neg bf16, x -> y at the planned offsets", "bytes_per_launch": nb,
+                       "ms_per_launch": round(cms, 5), "GB/s": round(nb / cms / 1e6, 1),
+                       "frac": round(nb / cms / 1e6 / HBM_PEAK_GBS, 4)}
+    if want_extras:
+        variants, mix = extras(rn, kept, args.steps, args.warmup)
+    del kept
+    torch.cuda.empty_cache()
     companions = []
-    if not args.no_companion and args.workload == HEADLINE:
+    if companions_wanted:
         for name in COMPANIONS:
             wc = synth.WORKLOADS[name]
-            cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True)
+            cinp = comp_inputs.pop(name, None)
+            cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True, inp=cinp,
+                                           arena=arena, placement=plans.get(name))
+            del cinp
             cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
             log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
             ci = rn.describe_launch(wc.B, wc.L, wc.D, flags_of(rn, wc), wc.op == "fused",
                                     wc.gate_layout or (0, 0), wc.ss_layout)
-            companions.append({"workload": wc.name, "ms_per_launch": round(cms, 5),
-                               "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
-                               "algorithmic_bytes": wc.algorithmic_bytes(),
-                               "traffic": measured_traffic(wc.name), "launch_ms": cstats,
-                               "launch": ci})
+            entry = {"workload": wc.name, "ms_per_launch": round(cms, 5),
+                     "GB/s": round(cg, 1), "frac": round(cg / HBM_PEAK_GBS, 4),
+                     "algorithmic_bytes": wc.algorithmic_bytes(),
+                     "traffic": measured_traffic(wc.name), "launch_ms": cstats,
+                     "launch": ci}
+            if name in plans:
+                entry["placement"] = plans[name].describe()
+            companions.append(entry)
+    if arena is not None:
+        arena.release()
+        arena = None
+        torch.cuda.empty_cache()
     info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused",
                               wl.gate_layout or (0, 0), wl.ss_layout)
     ref = copy_reference(args.steps, args.warmup, dev)
@@ -475,11 +628,14 @@ def main():
                    "algorithmic_bytes": nbytes, "launch": info},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)},
+        "placement": placement,
         "wall_s_timed_region": round(wall, 4),
         "launch_ms": per_launch,
         "companions": companions,
         "copy_reference": ref,
     }
+    if copy_placed is not None:
+        line["copy_reference_placed"] = copy_placed
     if want_extras:
         line["variants"] = variants
         line["dit_forward_mix"] = mix

@@ -1,0 +1,201 @@
+"""Placement of the row operations' activation tensors in HBM (MI355X).
+
+The row kernels stream every input once and write every output once, so
+their rate is set by HBM.  On MI355X that rate also depends on where the
+tensors sit in device memory, not only on how the kernel accesses them.
+Measured with the fused LayerNorm kernel at B 1, L 176400, D 5120 (four
+1.8 GB streams: x and residual read, y and residual_out written) placed at
+controlled offsets of one large allocation:
+
+  * the device address space splits into 32 GiB granules.  Within a granule
+    the rate does not depend on the offset of a tensor (0.25 to 32 MB shifts:
+    no effect), but each granule falls into one of a few classes;
+  * both output streams in granules of one class: 74-76 % of 8 TB/s.  That is
+    the case for tensors allocated back to back (they share a granule), which
+    is what a caching allocator gives on a fresh device;
+  * the inputs in one class and each output in its own other class: 82-83 %.
+    Other assignments fall in between (79-81 %);
+  * the pattern holds for the other workloads measured (the fused op at
+    L 90000 D 5120 and at D 10240 with per-row scale/shift, the norm-only op).
+
+The driver does not expose the classes, so `plan` measures them.  It packs
+the inputs into one granule, tries every assignment of the outputs to other
+granules (with two choices of the input granule), times the actual launch
+for each, times the three fastest again with more launches, and keeps the
+fastest of those.  About 100 short trials take 1-3 s.
+
+`HbmArena` owns one allocation that spans whole granules of the free
+device memory; callers take typed views of it at the offsets a `Placement`
+gives.  The kernels themselves are unchanged; this module only decides where
+their operands live.  It uses torch for the device allocation and for event
+timing.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from dataclasses import dataclass, field
+
+GRANULE = 32 << 30          # bytes of device address space that share one class
+SLOT_START = 8 << 30        # first byte used inside a granule (clear of its edges)
+SLOT_SPAN = 16 << 30        # bytes usable per granule from SLOT_START
+ALIGN = 2 << 20             # tensors start on 2 MiB boundaries
+
+
+def round_up(n: int, a: int = ALIGN) -> int:
+    return (int(n) + a - 1) // a * a
+
+
+def candidates(n_granules: int, n_writes: int, read_granules: int = 2):
+    """Every (read granule, write granules) assignment the planner tries: the
+    inputs in one of the first `read_granules` granules, each output in its
+    own granule, all distinct."""
+    if n_writes < 1:
+        raise ValueError("a placement needs at least one output tensor")
+    if n_granules < n_writes + 1:
+        raise ValueError("%d granules cannot hold the inputs and %d outputs apart"
+                         % (n_granules, n_writes))
+    for rg in range(min(read_granules, n_granules)):
+        others = [g for g in range(n_granules) if g != rg]
+        for wg in itertools.permutations(others, n_writes):
+            yield rg, tuple(wg)
+
+
+def offsets(read_granule: int, write_granules, read_bytes, write_bytes):
+    """Byte offsets in the arena: the inputs packed from SLOT_START of the read
+    granule, each output group from SLOT_START of its own granule.
+
+    write_bytes[i] is either the size of output i or a list of sizes (outputs
+    that share output i's granule, packed in order)."""
+    if sum(round_up(b) for b in read_bytes) > SLOT_SPAN:
+        raise ValueError("the inputs (%d bytes) do not fit one granule's slot span" % sum(read_bytes))
+    reads, at = [], read_granule * GRANULE + SLOT_START
+    for b in read_bytes:
+        reads.append(at)
+        at += round_up(b)
+    writes = []
+    for g, group in zip(write_granules, write_bytes):
+        sizes = group if isinstance(group, (list, tuple)) else [group]
+        if sum(round_up(b) for b in sizes) > SLOT_SPAN:
+            raise ValueError("an output group (%d bytes) does not fit one granule's slot span" % sum(sizes))
+        at = g * GRANULE + SLOT_START
+        offs = []
+        for b in sizes:
+            offs.append(at)
+            at += round_up(b)
+        writes.append(offs if isinstance(group, (list, tuple)) else offs[0])
+    return reads, writes
+
+
+def choose(trials):
+    """The fastest trial of (ms, read_granule, write_granules); ties keep the
+    earlier one."""
+    best = None
+    for t in trials:
+        if best is None or t[0] < best[0]:
+            best = t
+    if best is None:
+        raise ValueError("no trials")
+    return best
+
+
+@dataclass
+class Placement:
+    read_granule: int
+    write_granules: tuple
+    read_offsets: list
+    write_offsets: list
+    ms: float                      # mean launch time of the chosen assignment
+    candidates: int = 0            # assignments timed in the first pass
+    trials: list = field(default_factory=list)   # (ms, read_granule, write_granules), both passes
+
+    def describe(self) -> dict:
+        first = self.trials[:self.candidates] or [(self.ms,)]
+        return {"granule_gib": GRANULE >> 30, "read_granule": self.read_granule,
+                "write_granules": list(self.write_granules), "candidates": self.candidates,
+                "refined": len(self.trials) - self.candidates, "ms_chosen": round(self.ms, 5),
+                "ms_first_pass_best": round(min(t[0] for t in first), 5),
+                "ms_first_pass_worst": round(max(t[0] for t in first), 5)}
+
+
+class HbmArena:
+    """One device allocation spanning whole granules of free HBM."""
+
+    def __init__(self, device=None, granules: int | None = None, keep_free: int = 24 << 30):
+        import torch
+        self._torch = torch
+        self.device = torch.device(device if device is not None else "cuda:0")
+        free, _ = torch.cuda.mem_get_info(self.device)
+        avail = max(0, (free - keep_free) // GRANULE)
+        n = avail if granules is None else min(int(granules), avail)
+        if n < 2:
+            raise RuntimeError("HbmArena needs at least two %d GiB granules of free device memory "
+                               "(%.1f GiB free, %d GiB kept free)" % (GRANULE >> 30, free / 2**30,
+                                                                      keep_free >> 30))
+        self.granules = int(n)
+        self.buf = torch.empty(self.granules * GRANULE, dtype=torch.uint8, device=self.device)
+
+    @property
+    def nbytes(self) -> int:
+        return self.buf.numel()
+
+    def view(self, offset: int, shape, dtype):
+        """A typed view of `shape` at byte `offset` (256-byte aligned, in bounds)."""
+        torch = self._torch
+        n = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+        if offset < 0 or offset % 256 or offset + n > self.nbytes:
+            raise ValueError("view of %d bytes at offset %d is outside the arena (%d bytes) or "
+                             "not 256-byte aligned" % (n, offset, self.nbytes))
+        return self.buf[offset:offset + n].view(dtype).view(*shape)
+
+    def release(self):
+        self.buf = None
+
+
+def plan(arena: HbmArena, read_bytes, write_bytes, make_launch, read_granules: int = 2,
+         steps: int = 6, warmup: int = 2, refine: int = 3, refine_steps: int = 24,
+         stream=None) -> Placement:
+    """Measure every candidate assignment and return the fastest.
+
+    make_launch(read_offsets, write_offsets) returns a zero-argument callable
+    that enqueues the operation on views of `arena` at those offsets.  Every
+    candidate is timed over `steps` launches; the `refine` fastest are timed
+    again over `refine_steps` launches and the choice is made on those, so that
+    a short trial's noise does not decide it.  Each input region is
+    zero-filled before it is first timed, so that no trial reads uninitialised
+    memory."""
+    torch = arena._torch
+    st = stream if stream is not None else torch.cuda.current_stream(arena.device)
+
+    def timed(rg, wg, n):
+        r_off, w_off = offsets(rg, wg, read_bytes, write_bytes)
+        call = make_launch(r_off, w_off)
+        for _ in range(warmup):
+            call()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        for _ in range(n):
+            call()
+        b.record(st)
+        b.synchronize()
+        return a.elapsed_time(b) / n
+
+    trials, filled = [], set()
+    for rg, wg in candidates(arena.granules, len(write_bytes), read_granules):
+        if rg not in filled:
+            r_off, _ = offsets(rg, wg, read_bytes, write_bytes)
+            for off, nb in zip(r_off, read_bytes):
+                arena.buf[off:off + nb].zero_()
+            filled.add(rg)
+        trials.append((timed(rg, wg, steps), rg, wg))
+    finals = [(timed(rg, wg, refine_steps), rg, wg) for _, rg, wg in sorted(trials, key=lambda t: t[0])[:refine]]
+    ms, rg, wg = choose(finals)
+    r_off, w_off = offsets(rg, wg, read_bytes, write_bytes)
+    return Placement(rg, wg, r_off, w_off, ms, len(trials), trials + finals)
+
+
+def launches(n_trials: int, refine: int = 3, steps: int = 6, warmup: int = 2,
+             refine_steps: int = 24) -> int:
+    """Kernel launches `plan` makes for `n_trials` candidates (with its defaults)."""
+    return n_trials * (warmup + steps) + min(refine, n_trials) * (warmup + refine_steps)

@@ -1,0 +1,79 @@
+"""The HBM placement planner's host logic (no GPU): the assignments it tries,
+the offsets it hands out, and the choice of the fastest trial."""
+import itertools
+
+import pytest
+
+from rmsnorm_diffusion_transformers_amd import hbm
+
+G = hbm.GRANULE
+
+
+def test_candidates_cover_every_distinct_assignment():
+    c = list(hbm.candidates(8, 2))
+    # inputs in granule 0 or 1; two outputs in distinct other granules
+    assert len(c) == 2 * 7 * 6
+    assert len(set(c)) == len(c)
+    for rg, wg in c:
+        assert rg in (0, 1) and len(wg) == 2
+        assert len({rg, *wg}) == 3
+    assert set(c) == {(rg, wg) for rg in (0, 1)
+                      for wg in itertools.permutations([g for g in range(8) if g != rg], 2)}
+    assert len(list(hbm.candidates(8, 1))) == 2 * 7
+    assert len(list(hbm.candidates(3, 2, read_granules=1))) == 2
+
+
+def test_candidates_refuse_too_few_granules():
+    with pytest.raises(ValueError):
+        list(hbm.candidates(2, 2))
+    with pytest.raises(ValueError):
+        list(hbm.candidates(4, 0))
+
+
+def test_offsets_pack_inputs_and_separate_outputs():
+    nb = 176400 * 5120 * 2
+    reads, writes = hbm.offsets(1, (5, 3), [nb, nb], [[nb, 2 * nb, nb // 2], nb])
+    a = hbm.round_up(nb)
+    assert reads == [G + hbm.SLOT_START, G + hbm.SLOT_START + a]
+    assert writes[0] == [5 * G + hbm.SLOT_START, 5 * G + hbm.SLOT_START + a,
+                         5 * G + hbm.SLOT_START + a + hbm.round_up(2 * nb)]
+    assert writes[1] == 3 * G + hbm.SLOT_START
+    # every region inside its granule's slot span and 2 MiB aligned; no overlaps
+    regions = [(reads[0], nb), (reads[1], nb), (writes[0][0], nb), (writes[0][1], 2 * nb),
+               (writes[0][2], nb // 2), (writes[1], nb)]
+    for off, n in regions:
+        g = off // G
+        assert off % hbm.ALIGN == 0
+        assert g * G + hbm.SLOT_START <= off and off + n <= g * G + hbm.SLOT_START + hbm.SLOT_SPAN
+    regions.sort()
+    for (o1, n1), (o2, _) in zip(regions, regions[1:]):
+        assert o1 + n1 <= o2
+
+
+def test_offsets_refuse_oversized_groups():
+    with pytest.raises(ValueError):
+        hbm.offsets(0, (1,), [hbm.SLOT_SPAN // 2 + 1, hbm.SLOT_SPAN // 2 + 1], [8])
+    with pytest.raises(ValueError):
+        hbm.offsets(0, (1,), [8], [[hbm.SLOT_SPAN, 1]])
+
+
+def test_choose_takes_the_fastest_and_the_first_of_ties():
+    trials = [(1.2, 0, (1, 2)), (1.1, 0, (2, 3)), (1.1, 1, (3, 4)), (1.3, 1, (0, 2))]
+    assert hbm.choose(trials) == (1.1, 0, (2, 3))
+    with pytest.raises(ValueError):
+        hbm.choose([])
+
+
+def test_describe_reports_the_search():
+    p = hbm.Placement(1, (4, 6), [0], [0, 0], 1.12, 2,
+                      [(1.1, 1, (4, 6)), (1.2, 0, (1, 2)), (1.12, 1, (4, 6))])
+    d = p.describe()
+    assert d == {"granule_gib": 32, "read_granule": 1, "write_granules": [4, 6], "candidates": 2,
+                 "refined": 1, "ms_chosen": 1.12, "ms_first_pass_best": 1.1,
+                 "ms_first_pass_worst": 1.2}
+
+
+def test_launch_count_of_a_search():
+    # 84 candidates x (2 + 6) launches, then the 3 fastest x (2 + 24)
+    assert hbm.launches(84) == 84 * 8 + 3 * 26
+    assert hbm.launches(2) == 2 * 8 + 2 * 26

@@ -1,0 +1,69 @@
+"""The HBM arena and the measured placement on the GPU: a planned placement
+changes where the operands live, never the results."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import compare_outputs, log, require_gpu, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def test_planned_placement_gives_the_same_bits():
+    import torch
+
+    require_gpu()
+    import rmsnorm_diffusion_transformers_amd as rn
+    from rmsnorm_diffusion_transformers_amd import hbm
+
+    B, L, D, F = 1, 4096, 5120, 4
+    log("hbm placement: fused LN per-frame B %d L %d D %d F %d, 3-granule arena" % (B, L, D, F))
+    x = synth.random_bf16((L, D), seed=21, tensor=synth.X)
+    r = synth.random_bf16((L, D), seed=21, tensor=synth.RES)
+    g = synth.random_bf16((F, D), seed=21, tensor=synth.GATE, dist=synth.UNIFORM)
+    sc = synth.random_bf16((F, D), seed=21, tensor=synth.SCALE, b=0.1)
+    sh = synth.random_bf16((F, D), seed=21, tensor=synth.SHIFT, b=0.1)
+    dg, dsc, dsh = to_dev(g), to_dev(sc), to_dev(sh)
+    lay = (rn.RN_FRAME, F)
+    stream = torch.cuda.current_stream()
+
+    def run(xd, rd, yd, od):
+        rn.resnorm_fused_fwd(yd, od, xd, rd, dg, None, None, dsc, dsh, B, L, D, rn.RN_GATE,
+                             lay, lay, 1e-6, stream)
+
+    # torch's own allocations
+    xd, rd = to_dev(x), to_dev(r)
+    yd, od = torch.empty_like(xd), torch.empty_like(xd)
+    run(xd, rd, yd, od)
+    torch.cuda.synchronize()
+    y_ref, ro_ref = to_host(yd), to_host(od)
+
+    arena = hbm.HbmArena(granules=3)
+    nb = L * D * 2
+    bf = torch.bfloat16
+
+    def make_launch(r_off, w_off):
+        v = [arena.view(o, (L, D), bf) for o in (*r_off, *w_off)]
+        return lambda: run(*v)
+
+    pl = hbm.plan(arena, [nb, nb], [nb, nb], make_launch, stream=stream)
+    assert pl.candidates == 4 and len(pl.trials) == 7 and pl.read_granule in (0, 1)
+    assert len({pl.read_granule, *pl.write_granules}) == 3
+    xa, ra = (arena.view(o, (L, D), bf) for o in pl.read_offsets)
+    ya, oa = (arena.view(o, (L, D), bf) for o in pl.write_offsets)
+    xa.copy_(xd)
+    ra.copy_(rd)
+    ya.fill_(float("nan"))
+    oa.fill_(float("nan"))
+    run(xa, ra, ya, oa)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(oa), ro_ref)
+    assert np.array_equal(to_host(ya), y_ref)
+    # and against the oracle on the placed outputs
+    y_o, ro_o, _ = oracle.Oracle().fused(x, r, g, None, None, sc, sh, B, L, D, False,
+                                         gate_layout=(2, F), ss_layout=(2, F), threads=8)
+    compare_outputs(to_host(ya), y_o, to_host(oa), ro_o, what="placed")
+    del xa, ra, ya, oa
+    arena.release()
+    torch.cuda.empty_cache()
