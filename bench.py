@@ -32,7 +32,8 @@ reference; and the CPU oracle baseline.
 Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
 GPU), --steps K, --warmup W, --placement planned|default, --calibrate (time a
 plain elementwise copy, used to scale rocprof byte counters), --no-cpu-baseline,
---no-extras, --workload NAME.
+--no-extras, --workload NAME, --placement-map (the granule class map of the
+headline kernel, one JSON line).
 """
 from __future__ import annotations
 
@@ -433,6 +434,83 @@ def copy_reference(steps, warmup, dev):
             "frac": round(4 * n / ms / 1e6 / HBM_PEAK_GBS, 4)}
 
 
+def placement_map(rn, dev, granules=7):
+    """Rate of the headline kernel for every assignment of x, residual, y and
+    residual_out to distinct granules of an HBM arena (the first `granules`
+    of it), a fixed reference placement timed every 40 assignments for drift;
+    then the granule classes inferred from which output pairs are slow, and
+    the rates grouped by class pattern.  Prints one JSON line."""
+    import itertools
+    import statistics
+
+    import torch
+
+    import synth
+    from rmsnorm_diffusion_transformers_amd import hbm
+    wl = synth.WORKLOADS[HEADLINE]
+    R, D = wl.R, wl.D
+    inp = make_inputs(wl)
+    arena = hbm.HbmArena(dev)
+    n = min(granules, arena.granules)
+    nb = R * D * 2
+    slot = lambda g: arena.view(g * hbm.GRANULE + hbm.SLOT_START, (R, D), torch.bfloat16)  # noqa: E731
+    views = [slot(g) for g in range(n)]
+    small = upload({k: inp[k] for k in ("gate", "scale", "shift")}, dev)
+    for v in views:
+        v.copy_(host_bf16(inp["x"]))
+    stream = torch.cuda.current_stream()
+
+    def rate(x, r, y, o, steps=16):
+        call = lambda: launch_workload(rn, wl, dict(small, x=x, residual=r), y, o, stream)  # noqa: E731
+        ms, _ = time_calls(call, steps, 3)
+        return wl.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    ref_place = (0, 0, 1, 2)
+    ref_views = (views[0], arena.view(hbm.SLOT_START + hbm.round_up(nb), (R, D), torch.bfloat16),
+                 views[1], views[2])
+    ref_views[1].copy_(host_bf16(inp["residual"]))
+    rows, refs = [], []
+    t0 = time.time()
+    for k, (gx, gr, gy, go) in enumerate(itertools.permutations(range(n), 4)):
+        if k % 40 == 0:
+            refs.append(rate(*ref_views))
+        rows.append(((gx, gr, gy, go), rate(views[gx], views[gr], views[gy], views[go])))
+    log("placement map: %d assignments in %.0f s" % (len(rows), time.time() - t0))
+    # output pairs: mean rate over assignments with {y, o} = {i, j}
+    pair = {}
+    for (gx, gr, gy, go), f in rows:
+        pair.setdefault(tuple(sorted((gy, go))), []).append(f)
+    pair = {k: statistics.mean(v) for k, v in pair.items()}
+    lo, hi = min(pair.values()), max(pair.values())
+    cut = (lo + hi) / 2
+    cls = list(range(n))
+
+    def find(a):
+        while cls[a] != a:
+            a = cls[a]
+        return a
+    for (i, j), f in pair.items():
+        if f < cut:
+            cls[find(i)] = find(j)
+    labels = {}
+    names = [labels.setdefault(find(g), "ABCDEFGH"[len(labels)]) for g in range(n)]
+    groups = {}
+    for (gx, gr, gy, go), f in rows:
+        groups.setdefault("".join(names[g] for g in (gx, gr, gy, go)), []).append(f)
+    patterns = sorted(((statistics.mean(v), k, len(v), min(v), max(v)) for k, v in groups.items()),
+                      reverse=True)
+    rows.sort(key=lambda t: t[1])
+    out = {"workload": wl.name, "granule_gib": hbm.GRANULE >> 30, "granules": n,
+           "assignments": len(rows), "reference_frac": [round(min(refs), 4), round(max(refs), 4)],
+           "output_pair_cut": round(cut, 4), "granule_class": names,
+           "patterns_x_r_y_o": [{"pattern": k, "n": c, "mean": round(m, 4), "min": round(a, 4),
+                                 "max": round(b, 4)} for m, k, c, a, b in patterns],
+           "slowest": [[list(p), round(f, 4)] for p, f in rows[:5]],
+           "fastest": [[list(p), round(f, 4)] for p, f in rows[-5:]]}
+    arena.release()
+    print(json.dumps(out), flush=True)
+
+
 def calibrate(steps, warmup, dev):
     print(json.dumps(copy_reference(steps, warmup, dev)), flush=True)
 
@@ -499,6 +577,9 @@ def main():
                     help="planned: streamed tensors in an HBM arena at measured offsets; "
                          "default: torch's own allocations")
     ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--placement-map", action="store_true",
+                    help="time the headline kernel on every assignment of its four streamed "
+                         "tensors to distinct HBM granules and print the class map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-companion", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -518,6 +599,9 @@ def main():
     import rmsnorm_diffusion_transformers_amd as rn
     import synth
     from rmsnorm_diffusion_transformers_amd import hbm
+    if args.placement_map:
+        placement_map(rn, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     want_extras = not args.no_extras and args.workload == HEADLINE
     companions_wanted = not args.no_companion and args.workload == HEADLINE
