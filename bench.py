@@ -627,22 +627,33 @@ def main():
                                            "frac": round(dg / HBM_PEAK_GBS, 4)}
         try:
             arena = hbm.HbmArena(dev)
+            if arena.granules < 3:
+                raise RuntimeError("only %d granules of free HBM" % arena.granules)
         except RuntimeError as e:
             log("no HBM arena (%s); torch allocations are used" % e)
             placement["note"] = str(e)
+            arena = None
+            torch.cuda.empty_cache()
     if arena is not None:
-        placement["kind"] = "planned"
         placement["arena_granules"] = arena.granules
-        pl, info = plan_workload(rn, wl, inp, arena, dev, extra_bytes)
-        plans[wl.name] = pl
-        placement.update(info)
-        prelude += hbm.launches(pl.candidates)
+        try:
+            pl, info = plan_workload(rn, wl, inp, arena, dev, extra_bytes)
+            plans[wl.name] = pl
+            placement["kind"] = "planned"
+            placement.update(info)
+            prelude += hbm.launches(pl.candidates)
+        except ValueError as e:
+            log("%s: no placement (%s); torch allocations are used" % (wl.name, e))
+            placement["note"] = str(e)
         if companions_wanted:
             for name in COMPANIONS:
                 wc = synth.WORKLOADS[name]
                 comp_inputs[name] = make_inputs(wc)
-                plans[name], _ = plan_workload(rn, wc, comp_inputs[name], arena, dev)
-                prelude += hbm.launches(plans[name].candidates)
+                try:
+                    plans[name], _ = plan_workload(rn, wc, comp_inputs[name], arena, dev)
+                    prelude += hbm.launches(plans[name].candidates)
+                except ValueError as e:
+                    log("%s: no placement (%s); torch allocations are used" % (name, e))
     log("row-kernel launches before the timed workloads: %d" % prelude)
 
     pl = plans.get(wl.name)
