@@ -161,31 +161,30 @@ def host_bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
 
 
-def plan_workload(rn, wl, inp, arena, dev, extra_out_bytes=()):
+def plan_workload(rn, wl, inp, arena, dev, extra_out=()):
     """Measured placement of the workload's streamed inputs and its outputs in
-    the arena (rmsnorm_diffusion_transformers_amd.hbm.plan); extra outputs
-    share y's granule."""
+    the arena (rmsnorm_diffusion_transformers_amd.hbm.place_streams); the
+    extra outputs, given as (shape, dtype), share y's granule."""
     import torch
 
     from rmsnorm_diffusion_transformers_amd import hbm
     keys = streamed_keys(wl)
     small = upload({k: v for k, v in inp.items() if k not in keys}, dev)
-    nb = wl.R * wl.D * 2
-    writes = [[nb, *extra_out_bytes] if extra_out_bytes else nb] + ([nb] if wl.op == "fused" else [])
-    stream = torch.cuda.current_stream()
     shape = inp["x"].shape
+    bf = torch.bfloat16
+    y_spec = [(shape, bf), *extra_out] if extra_out else (shape, bf)
+    outputs = [y_spec] + ([(shape, bf)] if wl.op == "fused" else [])
+    stream = torch.cuda.current_stream()
 
-    def make_launch(r_off, w_off):
-        d = dict(small)
-        for k, off in zip(keys, r_off):
-            d[k] = arena.view(off, inp[k].shape, torch.bfloat16)
-        y_off = w_off[0][0] if isinstance(w_off[0], list) else w_off[0]
-        y = arena.view(y_off, shape, torch.bfloat16)
-        ro = arena.view(w_off[1], shape, torch.bfloat16) if wl.op == "fused" else None
+    def make_launch(ins, outs):
+        d = dict(small, **dict(zip(keys, ins)))
+        y = outs[0][0] if extra_out else outs[0]
+        ro = outs[1] if wl.op == "fused" else None
         return lambda: launch_workload(rn, wl, d, y, ro, stream)
 
     t0 = time.time()
-    pl = hbm.plan(arena, [inp[k].nbytes for k in keys], writes, make_launch, stream=stream)
+    _, _, pl = hbm.place_streams(arena, [(inp[k].shape, bf) for k in keys], outputs, make_launch,
+                                 stream=stream)
     info = pl.describe()
     info["search_s"] = round(time.time() - t0, 2)
     log("%s: placement inputs @ granule %d, outputs @ %s (%d candidates %.4f..%.4f ms, chosen %.4f ms, "
@@ -608,7 +607,6 @@ def main():
     nbytes = wl.algorithmic_bytes()
     inp = make_inputs(wl)
     extra_out = [((wl.R, wl.D), torch.float32), ((wl.R, wl.D), torch.float8_e4m3fn)] if want_extras else []
-    extra_bytes = [wl.R * wl.D * 4, wl.R * wl.D] if want_extras else []
 
     # Row-kernel launches before the timed workloads (the default-allocation
     # pass and the placement trials), so that a kernel trace can be split.
@@ -637,7 +635,7 @@ def main():
     if arena is not None:
         placement["arena_granules"] = arena.granules
         try:
-            pl, info = plan_workload(rn, wl, inp, arena, dev, extra_bytes)
+            pl, info = plan_workload(rn, wl, inp, arena, dev, extra_out)
             plans[wl.name] = pl
             placement["kind"] = "planned"
             placement.update(info)

@@ -199,3 +199,41 @@ def launches(n_trials: int, refine: int = 3, steps: int = 6, warmup: int = 2,
              refine_steps: int = 24) -> int:
     """Kernel launches `plan` makes for `n_trials` candidates (with its defaults)."""
     return n_trials * (warmup + steps) + min(refine, n_trials) * (warmup + refine_steps)
+
+
+def place_streams(arena: HbmArena, inputs, outputs, make_launch, **plan_kw):
+    """Plan a placement and return typed views at it: (input views, output
+    views, Placement).
+
+    inputs: list of (shape, dtype) of the tensors the operation reads once per
+    launch (packed into one granule).  outputs: list whose items are either a
+    (shape, dtype) or a list of them (outputs that share one granule, such as a
+    second output dtype written instead of the first).  make_launch(in_views,
+    out_views) returns a zero-argument callable that enqueues the operation;
+    out_views mirrors `outputs` (a list where a group was given).  Keyword
+    arguments go to `plan`."""
+    torch = arena._torch
+
+    def nbytes(spec):
+        shape, dtype = spec
+        return math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+
+    def is_group(o):
+        return isinstance(o, list)
+
+    read_bytes = [nbytes(i) for i in inputs]
+    write_bytes = [[nbytes(x) for x in o] if is_group(o) else nbytes(o) for o in outputs]
+
+    def views(r_off, w_off):
+        ins = [arena.view(off, shape, dt) for off, (shape, dt) in zip(r_off, inputs)]
+        outs = []
+        for off, o in zip(w_off, outputs):
+            if is_group(o):
+                outs.append([arena.view(a, shape, dt) for a, (shape, dt) in zip(off, o)])
+            else:
+                outs.append(arena.view(off, o[0], o[1]))
+        return ins, outs
+
+    pl = plan(arena, read_bytes, write_bytes, lambda r, w: make_launch(*views(r, w)), **plan_kw)
+    ins, outs = views(pl.read_offsets, pl.write_offsets)
+    return ins, outs, pl

@@ -40,18 +40,24 @@ def test_planned_placement_gives_the_same_bits():
     y_ref, ro_ref = to_host(yd), to_host(od)
 
     arena = hbm.HbmArena(granules=3)
-    nb = L * D * 2
     bf = torch.bfloat16
 
-    def make_launch(r_off, w_off):
-        v = [arena.view(o, (L, D), bf) for o in (*r_off, *w_off)]
-        return lambda: run(*v)
+    def make_launch(ins, outs):
+        return lambda: run(ins[0], ins[1], outs[0][0], outs[1])
 
-    pl = hbm.plan(arena, [nb, nb], [nb, nb], make_launch, stream=stream)
+    # y shares its granule with a binary32 tensor of the same shape (as a
+    # second output type would); residual_out gets its own granule
+    (xa, ra), (ygroup, oa), pl = hbm.place_streams(
+        arena, [((L, D), bf), ((L, D), bf)], [[((L, D), bf), ((L, D), torch.float32)], ((L, D), bf)],
+        make_launch, stream=stream)
+    ya, y32 = ygroup
     assert pl.candidates == 4 and len(pl.trials) == 7 and pl.read_granule in (0, 1)
     assert len({pl.read_granule, *pl.write_granules}) == 3
-    xa, ra = (arena.view(o, (L, D), bf) for o in pl.read_offsets)
-    ya, oa = (arena.view(o, (L, D), bf) for o in pl.write_offsets)
+    base = arena.buf.data_ptr()
+    granule = lambda t: (t.data_ptr() - base) // hbm.GRANULE  # noqa: E731
+    assert y32.data_ptr() >= ya.data_ptr() + L * D * 2
+    assert granule(y32) == granule(ya) == pl.write_granules[0]
+    assert granule(oa) == pl.write_granules[1] and granule(xa) == granule(ra) == pl.read_granule
     xa.copy_(xd)
     ra.copy_(rd)
     ya.fill_(float("nan"))
@@ -64,6 +70,6 @@ def test_planned_placement_gives_the_same_bits():
     y_o, ro_o, _ = oracle.Oracle().fused(x, r, g, None, None, sc, sh, B, L, D, False,
                                          gate_layout=(2, F), ss_layout=(2, F), threads=8)
     compare_outputs(to_host(ya), y_o, to_host(oa), ro_o, what="placed")
-    del xa, ra, ya, oa
+    del xa, ra, ya, oa, y32, ygroup
     arena.release()
     torch.cuda.empty_cache()
