@@ -73,3 +73,50 @@ def test_planned_placement_gives_the_same_bits():
     del xa, ra, ya, oa, y32, ygroup
     arena.release()
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["fused_ln_frame_b1_f49_l176400_d5120", "nss_ln_b1_l176400_d5120"])
+def test_full_size_workload_on_a_planned_placement(name):
+    """Every row of a full-size workload with its streamed tensors at a planned
+    placement (as bench.py times it), against the oracle."""
+    import os
+
+    import torch
+
+    require_gpu()
+    import rmsnorm_diffusion_transformers_amd as rn
+    from rmsnorm_diffusion_transformers_amd import hbm
+    from gpu_util import launch_workload
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    wl = synth.WORKLOADS[name]
+    log("workload %s on a planned placement: generating inputs" % name)
+    inp = synth.make_inputs(wl, threads=threads)
+    fused = wl.op == "fused"
+    streamed = ["x", "residual"] if fused else ["x"]
+    small = {k: to_dev(v) for k, v in inp.items() if k not in streamed}
+    act = ((wl.R, wl.D), torch.bfloat16)
+    arena = hbm.HbmArena(granules=3)
+
+    def make_launch(ins, outs):
+        d = dict(small, **dict(zip(streamed, ins)))
+        return lambda: launch_workload(rn, wl, d, outs[0], outs[1] if fused else None)
+
+    ins, outs, pl = hbm.place_streams(arena, [act] * len(streamed), [act] * (2 if fused else 1),
+                                      make_launch)
+    log("placement: inputs @ %d, outputs @ %s" % (pl.read_granule, list(pl.write_granules)))
+    for k, v in zip(streamed, ins):
+        v.copy_(to_dev(inp[k]))
+    for o in outs:
+        o.fill_(float("nan"))
+    make_launch(ins, outs)()
+    torch.cuda.synchronize()
+    yh = to_host(outs[0])
+    roh = to_host(outs[1]) if fused else None
+    del ins, outs
+    arena.release()
+    torch.cuda.empty_cache()
+    log("workload %s: oracle on %d rows x %d threads" % (name, wl.R, threads))
+    y_ref, ro_ref, _ = oracle.Oracle().run_workload(wl, inp, threads=threads)
+    compare_outputs(yh, y_ref, roh, ro_ref, name + " (planned placement)")
+    log("workload %s on a planned placement: OK" % name)
