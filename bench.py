@@ -404,6 +404,23 @@ def small_batch_latency(rn, dev, names=("fused_ln_b1_l16_d5120", "fused_rms_w_b2
         log("%s: %.2f us/call on the stream, %.2f us/call in a graph" % (
             name, eager_ms * 1e3, graph_ms * 1e3 / 100))
         del g, d, y, ro
+    # the floor: a one-element torch.neg, 100 launches captured and replayed the same way
+    a = torch.zeros(1, device=dev)
+    b = torch.empty_like(a)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.neg(a, out=b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(100):
+            torch.neg(a, out=b)
+    floor_ms, _ = time_calls(g.replay, 20, 3)
+    out.append({"workload": "launch floor: one-element torch.neg", "us_per_call_graph": round(floor_ms * 1e3 / 100, 2)})
+    log("launch floor (one-element torch.neg in a graph): %.2f us/call" % (floor_ms * 1e3 / 100))
+    del g, a, b
     return out
 
 
