@@ -10,11 +10,11 @@ controlled offsets of one large allocation:
   * the device address space splits into 32 GiB granules.  Within a granule
     the rate does not depend on the offset of a tensor (0.25 to 32 MB shifts:
     no effect), but each granule falls into one of a few classes;
-  * both output streams in granules of one class: 74-76 % of 8 TB/s.  That is
+  * both output streams in granules of one class: 74-77 % of 8 TB/s.  That is
     the case for tensors allocated back to back (they share a granule), which
     is what a caching allocator gives on a fresh device;
   * the inputs in one class and each output in its own other class: 82-83 %.
-    Other assignments fall in between (79-81 %);
+    Other assignments fall in between (79-82 %);
   * the pattern holds for the other workloads measured (the fused op at
     L 90000 D 5120 and at D 10240 with per-row scale/shift, the norm-only op).
 
