@@ -198,12 +198,24 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   // row; a sweep of every shape at ~903 M elements, D = 5632-6144 and
   // 10752-12288: 2.3-6.5 % faster, e.g. D = 12288 0.638 -> 0.599 ms).
   const bool nss_plain = !fused && !(flags & RN_WEIGHT);
+  // Large norm-only problems run one-wave shapes of 8 or 10 vectors per lane
+  // with 2 rows per workgroup (the twins after the multi-row shapes).
+  auto rows2_twin = [&](int i) {
+    const rn::Shape s = rn::kShapes[i];
+    if (!(nss_plain && s.w == 1 && s.k == 1 && s.vpt >= 8 && R * D >= rn::kMultiRowMinElems)) return i;
+    for (int j = 0; j < rn::kNumShapes; ++j) {
+      const rn::Shape t = rn::kShapes[j];
+      if (t.w == s.w && t.vpt == s.vpt && t.k == 1 && t.rpb == 2) return j;
+    }
+    return i;
+  };
   int fallback = -1;
   for (int i = 0; i < rn::kNumShapes; ++i) {
     const rn::Shape s = rn::kShapes[i];
     if (s.k > 1 || s.w == 10 || !allowed(s) || !covers(s)) continue;
+    if (s.w == 1 && s.rpb != 4) continue;  // twins are chosen only through rows2_twin
     if (nss_plain && s.w >= 2 && s.vpt == 6) continue;
-    if (fits(s)) return i;
+    if (fits(s)) return rows2_twin(i);
     if (fallback < 0 || rn::kShapes[fallback].w < s.w) fallback = i;
   }
   return fallback;

@@ -54,6 +54,14 @@ constexpr int kWaveSize = 64;
 //     K = 8; prefetching the next row before the current row's stores did
 //     not help on balance.  The fused op and the norm-only op without
 //     affine ran slower as multi-row shapes.
+//   * the norm-only op without affine, from kMultiRowMinElems elements, runs
+//     its one-wave shapes of 8 or 10 vectors per lane with 2 rows per
+//     workgroup instead of 4 (the twins at the end of the table): with the
+//     tensors at a measured HBM placement, D = 5120 78.0 -> 79.5 % of 8 TB/s
+//     and D = 4096 78.8-79.6 -> 80.0 %; on back-to-back allocations within
+//     +-0.4 % at D = 5120 and 74.4 -> 75.6 % at D = 4096.  At 4 vectors per
+//     lane 2 rows per workgroup were slower (D = 2048: 81.1 -> 80.2 %), at 6
+//     the same.
 struct Shape {
   int w;
   int vpt;
@@ -61,7 +69,9 @@ struct Shape {
   int k = 1;  // consecutive rows per wave
 };
 // One-row shapes sorted by W, then VPT (the planner takes the first fit of a
-// given W), then the multi-row shapes in the same order.
+// given W), then the multi-row shapes in the same order, then twins of
+// one-row shapes with fewer rows per workgroup (never a first fit: they
+// follow shapes of the same W and VPT).
 constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1, 5, 4},
                              {1, 6, 4},  {1, 8, 4},  {1, 10, 4}, {2, 3, 2},  {2, 4, 2},
                              {2, 5, 2},  {2, 6, 2},  {2, 8, 2},  {2, 10, 2}, {4, 2, 1},
@@ -70,7 +80,9 @@ constexpr Shape kShapes[] = {{1, 1, 4},  {1, 2, 4},  {1, 3, 4},  {1, 4, 4},  {1,
                              // multi-row shapes (norm-only with weight)
                              {1, 1, 4, 4}, {1, 2, 4, 4}, {1, 3, 4, 4}, {1, 4, 4, 4},
                              {1, 5, 4, 4}, {2, 3, 2, 4}, {2, 4, 2, 4}, {2, 5, 2, 4},
-                             {4, 3, 1, 4}, {4, 4, 1, 4}, {4, 5, 1, 4}};
+                             {4, 3, 1, 4}, {4, 4, 1, 4}, {4, 5, 1, 4},
+                             // two rows per workgroup (large norm-only problems)
+                             {1, 8, 2}, {1, 10, 2}};
 constexpr int kManyStreamsMinD = 2560;
 constexpr int kSplitMinD = 2048;
 constexpr int kTinyRows = 128;

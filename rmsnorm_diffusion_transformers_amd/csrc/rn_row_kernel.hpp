@@ -719,13 +719,14 @@ KernelFn kernel_for_shape(int shape) {
     RN_CASE(15) RN_CASE(16) RN_CASE(17) RN_CASE(18) RN_CASE(19) RN_CASE(20) RN_CASE(21)
     RN_CASE(22) RN_CASE(23) RN_CASE(24) RN_CASE(25) RN_CASE(26) RN_CASE(27) RN_CASE(28)
     RN_CASE(29) RN_CASE(30) RN_CASE(31) RN_CASE(32) RN_CASE(33) RN_CASE(34)
+    RN_CASE(35) RN_CASE(36)
 #undef RN_CASE
     default:
       return nullptr;
   }
 }
 
-static_assert(kNumShapes == 35, "kernel_for_shape lists every shape");
+static_assert(kNumShapes == 37, "kernel_for_shape lists every shape");
 
 // Table of one (norm, op, gate, output) family over the affine variants.
 template <bool RMS, bool FUSED, bool GATE, int OUT>

@@ -639,3 +639,25 @@ def test_one_hip_runtime_whatever_the_import_order():
     libs = out.stdout.split()
     assert len([l for l in libs if "libamdhip64" in l]) == 1, libs
     assert len([l for l in libs if "libhsa-runtime64" in l]) == 1, libs
+
+
+def test_norm_only_two_rows_per_workgroup(rn):
+    """Large norm-only problems without affine run the one-wave shapes of 8 or
+    10 vectors per lane with 2 rows per workgroup; narrower rows, smaller
+    problems, the fused op and the norm-only op with weight keep their
+    shapes."""
+    i = rn.describe_launch(1, 176400, 5120, 0, False)
+    assert (i["waves_per_row"], i["vec_per_lane"], i["rows_per_block"], i["block_threads"]) == (1, 10, 2, 128)
+    assert i["grid_blocks"] == 176400 // 2
+    i = rn.describe_launch(1, 220500, 4096, 0, False)
+    assert (i["waves_per_row"], i["vec_per_lane"], i["rows_per_block"]) == (1, 8, 2)
+    for D in range(3592, 5121, 8):
+        i = rn.describe_launch(1, -(-(12 << 20) // D), D, rn.RN_RMS, False)
+        assert (i["waves_per_row"], i["rows_per_block"]) == (1, 2), D
+    for D in (2048, 3072):
+        i = rn.describe_launch(1, 903168000 // D, D, 0, False)
+        assert (i["waves_per_row"], i["rows_per_block"]) == (1, 4), D
+    # below 12 Mi elements, with weight, or fused: four rows per workgroup
+    assert rn.describe_launch(1, 2000, 5120, 0, False)["rows_per_block"] == 4
+    assert rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True)["rows_per_block"] == 4
+    assert rn.describe_launch(1, 176400, 5120, rn.RN_WEIGHT, False)["rows_per_wave"] == 4

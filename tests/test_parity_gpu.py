@@ -352,8 +352,8 @@ SHAPE_ROWS = ((2, 263), (2, 600), (2, 1031), (1, 8195), (1, 24579))
 
 def _shape_cases(rn):
     """One (B, L, D, fused, flags, scale/shift layout) per compiled (waves per
-    row, vectors per lane, rows per wave) shape, at the first row count and
-    row width that select it."""
+    row, vectors per lane, rows per wave, rows per workgroup) shape, at the
+    first row count and row width that select it."""
     seen = {}
     flag_sets = [(False, 0), (True, rn.RN_GATE), (True, rn.RN_GATE | rn.RN_WEIGHT),
                  (True, rn.RN_GATE | rn.RN_WEIGHT | rn.RN_BIAS), (False, rn.RN_WEIGHT | rn.RN_BIAS)]
@@ -363,22 +363,22 @@ def _shape_cases(rn):
                 for sl in ((BCAST, 0), (ROW, 0)):
                     gl = (FRAME, 1) if flags & rn.RN_GATE else (BCAST, 0)
                     i = rn.describe_launch(B, L, D, flags, fused, gl, sl)
-                    key = (i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"])
+                    key = (i["waves_per_row"], i["vec_per_lane"], i["rows_per_wave"], i["rows_per_block"])
                     if key not in seen:
                         seen[key] = (B, L, D, fused, flags, sl)
     return seen
 
 
 def test_every_compiled_shape(rn, orc):
-    """Every compiled (waves per row, vectors per lane, rows per wave) shape
-    the planner can pick, at the first row width that selects it (a ragged
+    """Every compiled (waves per row, vectors per lane, rows per wave, rows per
+    workgroup) shape the planner can pick, at the first row width that selects it (a ragged
     row for most), with odd L (so the last workgroup of a shape with several
     rows per workgroup is partly empty)."""
     cases = _shape_cases(rn)
-    assert len(cases) == 35, sorted(cases)
-    for (w, vpt, k), (B, L, D, fused, flags, sl) in sorted(cases.items()):
-        log("shape W=%d VPT=%d K=%d via B=%d L=%d D=%d fused=%s flags=%d ss=%s" % (
-            w, vpt, k, B, L, D, fused, flags, sl))
+    assert len(cases) == 37, sorted(cases)
+    for (w, vpt, k, rpb), (B, L, D, fused, flags, sl) in sorted(cases.items()):
+        log("shape W=%d VPT=%d K=%d rows/workgroup %d via B=%d L=%d D=%d fused=%s flags=%d ss=%s" % (
+            w, vpt, k, rpb, B, L, D, fused, flags, sl))
         aff = 2 if flags & rn.RN_BIAS else (1 if flags & rn.RN_WEIGHT else 0)
         gl = (FRAME, 1) if flags & rn.RN_GATE else None
         for rms in (False, True):
