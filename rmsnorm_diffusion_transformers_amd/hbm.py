@@ -22,7 +22,7 @@ The driver does not expose the classes, so `plan` measures them.  It packs
 the inputs into one granule, tries every assignment of the outputs to other
 granules (with two choices of the input granule), times the actual launch
 for each, times the three fastest again with more launches, and keeps the
-fastest of those.  About 100 short trials take 1-3 s.
+fastest of those: 0.1-1.3 s per workload for the ones measured (14-84 candidates).
 
 `HbmArena` owns one allocation that spans whole granules of the free
 device memory; callers take typed views of it at the offsets a `Placement`
@@ -149,6 +149,8 @@ class HbmArena:
         return self.buf[offset:offset + n].view(dtype).view(*shape)
 
     def release(self):
+        """Drop the arena's reference; the memory returns to torch once no view
+        of it is alive either."""
         self.buf = None
 
 
