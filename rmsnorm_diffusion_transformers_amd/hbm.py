@@ -42,7 +42,9 @@ SLOT_SPAN = 16 << 30        # bytes usable per granule from SLOT_START
 ALIGN = 2 << 20             # tensors start on 2 MiB boundaries
 
 
-def round_up(n: int, a: int = ALIGN) -> int:
+def round_up(n: int, a: int | None = None) -> int:
+    """n rounded up to a multiple of `a` (ALIGN unless given)."""
+    a = ALIGN if a is None else a
     return (int(n) + a - 1) // a * a
 
 

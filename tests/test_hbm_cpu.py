@@ -77,3 +77,55 @@ def test_launch_count_of_a_search():
     # 84 candidates x (2 + 6) launches, then the 3 fastest x (2 + 24)
     assert hbm.launches(84) == 84 * 8 + 3 * 26
     assert hbm.launches(2) == 2 * 8 + 2 * 26
+
+
+def test_place_streams_builds_typed_views(monkeypatch):
+    """place_streams hands out views at the offsets the plan chose: inputs
+    packed in the read granule, each output (or output group) in its own
+    granule, with the requested shapes and dtypes and no overlap.  Run on a
+    small CPU-backed arena with scaled-down granules and the timing replaced."""
+    import torch
+
+    monkeypatch.setattr(hbm, "GRANULE", 1 << 20)
+    monkeypatch.setattr(hbm, "SLOT_START", 1 << 18)
+    monkeypatch.setattr(hbm, "SLOT_SPAN", 1 << 19)
+    monkeypatch.setattr(hbm, "ALIGN", 1 << 12)
+
+    class Arena(hbm.HbmArena):
+        def __init__(self):
+            self._torch = torch
+            self.device = torch.device("cpu")
+            self.granules = 4
+            self.buf = torch.zeros(4 << 20, dtype=torch.uint8)
+
+    arena = Arena()
+    seen = {}
+
+    def fake_plan(ar, read_bytes, write_bytes, make_launch, **kw):
+        r_off, w_off = hbm.offsets(2, (0, 3), read_bytes, write_bytes)
+        seen["call"] = make_launch(r_off, w_off)
+        return hbm.Placement(2, (0, 3), r_off, w_off, 1.0, 1, [(1.0, 2, (0, 3))])
+
+    monkeypatch.setattr(hbm, "plan", fake_plan)
+    bf = torch.bfloat16
+    launched = []
+    ins, outs, pl = hbm.place_streams(
+        arena, [((64, 32), bf), ((64, 32), bf)],
+        [[((64, 32), bf), ((64, 32), torch.float32)], ((64, 32), bf)],
+        lambda i, o: (lambda: launched.append((i, o))))
+    seen["call"]()
+    assert len(launched) == 1 and pl.read_granule == 2
+    base = arena.buf.data_ptr()
+    off = lambda t: t.data_ptr() - base  # noqa: E731
+    assert [t.shape for t in ins] == [(64, 32), (64, 32)] and all(t.dtype == bf for t in ins)
+    assert off(ins[0]) == 2 * hbm.GRANULE + hbm.SLOT_START
+    assert off(ins[1]) == off(ins[0]) + hbm.round_up(64 * 32 * 2)
+    y, y32 = outs[0]
+    assert y.dtype == bf and y32.dtype == torch.float32 and y32.shape == (64, 32)
+    assert off(y) == hbm.SLOT_START and off(y32) == off(y) + hbm.round_up(64 * 32 * 2)
+    assert off(outs[1]) == 3 * hbm.GRANULE + hbm.SLOT_START
+    # writing through one view leaves every other view untouched
+    for t in (*ins, y, y32, outs[1]):
+        t.zero_()
+    y32.fill_(1.0)
+    assert all(float(t.abs().sum()) == 0 for t in (*ins, y, outs[1]))
