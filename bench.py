@@ -33,7 +33,8 @@ Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
 GPU), --steps K, --warmup W, --placement planned|default, --calibrate (time a
 plain elementwise copy, used to scale rocprof byte counters), --no-cpu-baseline,
 --no-extras, --workload NAME, --placement-map (the granule class map of the
-headline kernel, one JSON line).
+headline kernel, one JSON line), --placement-widths (torch's allocations against
+a planned placement at row widths 2048-10240, one JSON line).
 """
 from __future__ import annotations
 
@@ -527,6 +528,73 @@ def placement_map(rn, dev, granules=7):
     print(json.dumps(out), flush=True)
 
 
+def placement_widths(rn, dev, widths=(2048, 3072, 4096, 5120, 6144, 8192, 10240)):
+    """Fused LayerNorm (broadcast gate/scale/shift) and the norm-only op at
+    several row widths, 176400 x 5120 elements each: torch's own allocations
+    first, then one planned placement per problem (hbm.place_streams).  Prints
+    one JSON line."""
+    import numpy as np
+    import torch
+
+    from rmsnorm_diffusion_transformers_amd import hbm
+    total = 176400 * 5120
+    stream = torch.cuda.current_stream()
+    bf = torch.bfloat16
+    rng = np.random.default_rng(5)
+
+    def mods(D):
+        g = torch.from_numpy(rng.uniform(0, 1, (1, D)).astype(np.float32)).to(dev).to(bf)
+        sc = torch.from_numpy((0.1 * rng.standard_normal((1, D))).astype(np.float32)).to(dev).to(bf)
+        sh = torch.from_numpy((0.1 * rng.standard_normal((1, D))).astype(np.float32)).to(dev).to(bf)
+        return g, sc, sh
+
+    def fused(L, D, g, sc, sh):
+        return lambda x, r, y, o: (lambda: rn.resnorm_fused_fwd(
+            y, o, x, r, g, None, None, sc, sh, 1, L, D, rn.RN_GATE, (0, 0), (0, 0), 1e-6, stream))
+
+    def nss(L, D, sc, sh):
+        return lambda x, y: (lambda: rn.norm_scale_shift_fwd(
+            y, x, None, None, sc, sh, 1, L, D, 0, (0, 0), 1e-6, stream))
+
+    def frac(nbytes, call):
+        ms, _ = time_calls(call, 40, 8)
+        return round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    rows = {}
+    for D in widths:
+        L = total // D
+        g, sc, sh = mods(D)
+        x = torch.randn(L, D, device=dev).to(bf)
+        r = torch.randn(L, D, device=dev).to(bf)
+        y, o = torch.empty_like(x), torch.empty_like(x)
+        fi = rn.describe_launch(1, L, D, rn.RN_GATE, True)
+        ni = rn.describe_launch(1, L, D, 0, False)
+        rows[D] = {"rows": L, "fused_shape": [fi["waves_per_row"], fi["vec_per_lane"], fi["rows_per_block"]],
+                   "nss_shape": [ni["waves_per_row"], ni["vec_per_lane"], ni["rows_per_block"]],
+                   "fused_torch": frac(4 * L * D * 2, fused(L, D, g, sc, sh)(x, r, y, o)),
+                   "nss_torch": frac(2 * L * D * 2, nss(L, D, sc, sh)(x, y))}
+        del x, r, y, o
+        torch.cuda.empty_cache()
+    arena = hbm.HbmArena(dev)
+    for D in widths:
+        L = total // D
+        g, sc, sh = mods(D)
+        act = ((L, D), bf)
+        mk = fused(L, D, g, sc, sh)
+        (x, r), (y, o), _ = hbm.place_streams(arena, [act, act], [act, act],
+                                              lambda i, w: mk(i[0], i[1], w[0], w[1]), stream=stream)
+        x.normal_()
+        r.normal_()
+        rows[D]["fused_planned"] = frac(4 * L * D * 2, mk(x, r, y, o))
+        mkn = nss(L, D, sc, sh)
+        (xn,), (yn,), _ = hbm.place_streams(arena, [act], [act], lambda i, w: mkn(i[0], w[0]), stream=stream)
+        xn.normal_()
+        rows[D]["nss_planned"] = frac(2 * L * D * 2, mkn(xn, yn))
+        log("D %d: %s" % (D, rows[D]))
+    arena.release()
+    print(json.dumps({"elements": total, "widths": rows}), flush=True)
+
+
 def calibrate(steps, warmup, dev):
     print(json.dumps(copy_reference(steps, warmup, dev)), flush=True)
 
@@ -596,6 +664,9 @@ def main():
     ap.add_argument("--placement-map", action="store_true",
                     help="time the headline kernel on every assignment of its four streamed "
                          "tensors to distinct HBM granules and print the class map")
+    ap.add_argument("--placement-widths", action="store_true",
+                    help="torch's allocations against a planned placement for the fused and "
+                         "norm-only ops at several row widths")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-companion", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
@@ -617,6 +688,9 @@ def main():
     from rmsnorm_diffusion_transformers_amd import hbm
     if args.placement_map:
         placement_map(rn, dev)
+        return
+    if args.placement_widths:
+        placement_widths(rn, dev)
         return
     wl = synth.WORKLOADS[args.workload]
     want_extras = not args.no_extras and args.workload == HEADLINE
