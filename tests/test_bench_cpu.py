@@ -57,3 +57,15 @@ def test_committed_traffic_matches_current_sources():
                 assert kv["kernel_digest"] == bench.kernel_digest()
                 hbm, alg = int(kv["hbm_bytes_per_launch"]), int(kv["algorithmic_bytes"])
                 assert abs(hbm / alg - 1) < 0.005, line
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    """bench.py measures one GPU: --gpus N > 1 exits with status 2 and says why,
+    before anything touches a device."""
+    import subprocess
+    import sys
+    out = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert out.returncode == 2
+    assert "exactly one GPU" in out.stderr and "--gpus 2" in out.stderr
+    assert out.stdout == ""
