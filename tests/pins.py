@@ -600,19 +600,21 @@ def pin_golden_worked_rows(o):
     results follow exactly from the definition (residual ties to even, gate 0,
     1/2 and 2, eps inside the square root, the biased variance, uncentred
     RMSNorm, affine before modulation, per-frame and per-row operand rows, a
-    constant row).  Every bit of y and residual_out must match."""
-    from golden_cases import load_cases
-    for c in load_cases():
-        common = dict(B=c["B"], L=c["L"], D=c["D"], is_rms=c["norm"] == "rms",
-                      ss_layout=c["layout.ss"], eps=c["eps"])
-        if c["op"] == "fused":
-            y, ro, _ = o.fused(c["x"], c["residual"], c["gate"], c.get("weight"), c.get("bias"),
-                               c["scale"], c["shift"], gate_layout=c["layout.gate"], **common)
+    constant row, binary32 weight/bias and output, an FP8 row with its scale).
+    Every bit of y, residual_out and the FP8 scale must match."""
+    from golden_cases import run_oracle
+    for c in load_golden():
+        y, ro, ys = run_oracle(o, c)
+        if ro is not None:
             assert np.array_equal(ro.ravel(), c["expect.residual_out"]), c["name"]
-        else:
-            y, _ = o.nss(c["x"], c.get("weight"), c.get("bias"), c["scale"], c["shift"], **common)
         assert np.array_equal(y.ravel(), c["expect.y"]), c["name"]
+        if ys is not None:
+            assert np.array_equal(ys.ravel(), c["expect.y_scale"]), c["name"]
 
+
+def load_golden():
+    from golden_cases import load_cases
+    return load_cases()
 
 FAST_PINS = [pin_golden_worked_rows, pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
              pin_torch_norms, pin_layouts, pin_fused_is_nss_of_residual, pin_scale_invariance,

@@ -9,7 +9,7 @@ reproduce residual_out bit for bit and y within the contract's bar."""
 import numpy as np
 import pytest
 
-from golden_cases import load_cases
+from golden_cases import Y_DTYPES, load_cases, run_oracle
 from util import bf16_to_f64, check_y
 
 CASES = load_cases()
@@ -24,12 +24,16 @@ def _op_rows(lay, B, L):
 def test_fixture_is_consistent():
     """Sizes in every case agree with its layouts, so a bad fixture cannot pass
     silently."""
-    assert len(CASES) == 9
+    assert len(CASES) == 11
     for c in CASES:
         B, L, D = c["B"], c["L"], c["D"]
         n = B * L * D
         assert c["op"] in ("fused", "nss") and c["norm"] in ("layer", "rms"), c["name"]
         assert c["x"].size == n and c["expect.y"].size == n, c["name"]
+        assert c["affine"] in ("bf16", "f32") and c["out"] in Y_DTYPES, c["name"]
+        assert ("expect.y_scale" in c) == (c["out"] == "fp8"), c["name"]
+        if c["out"] == "fp8":
+            assert c["expect.y_scale"].size == B * L, c["name"]
         ss = _op_rows(c["layout.ss"], B, L) * D
         assert c["scale"].size == ss and c["shift"].size == ss, c["name"]
         for k in ("weight", "bias"):
@@ -43,16 +47,12 @@ def test_fixture_is_consistent():
 
 @pytest.mark.parametrize("case", CASES, ids=IDS)
 def test_oracle_reproduces_worked_rows(orc, case):
-    c = case
-    common = dict(B=c["B"], L=c["L"], D=c["D"], is_rms=c["norm"] == "rms",
-                  ss_layout=c["layout.ss"], eps=c["eps"])
-    if c["op"] == "fused":
-        y, ro, _ = orc.fused(c["x"], c["residual"], c["gate"], c.get("weight"), c.get("bias"),
-                             c["scale"], c["shift"], gate_layout=c["layout.gate"], **common)
-        np.testing.assert_array_equal(ro.ravel(), c["expect.residual_out"])
-    else:
-        y, _ = orc.nss(c["x"], c.get("weight"), c.get("bias"), c["scale"], c["shift"], **common)
-    np.testing.assert_array_equal(y.ravel(), c["expect.y"])
+    y, ro, ys = run_oracle(orc, case)
+    if ro is not None:
+        np.testing.assert_array_equal(ro.ravel(), case["expect.residual_out"])
+    np.testing.assert_array_equal(y.ravel(), case["expect.y"])
+    if ys is not None:
+        np.testing.assert_array_equal(ys.ravel(), case["expect.y_scale"])
 
 
 @pytest.mark.gpu
@@ -63,27 +63,43 @@ def test_hip_path_reproduces_worked_rows(case):
     dev = require_gpu()
     import rmsnorm_diffusion_transformers_amd as rn
     c = case
-    log("golden case %s: B %d L %d D %d %s/%s" % (c["name"], c["B"], c["L"], c["D"], c["op"], c["norm"]))
+    log("golden case %s: B %d L %d D %d %s/%s, affine %s, y %s" % (
+        c["name"], c["B"], c["L"], c["D"], c["op"], c["norm"], c["affine"], c["out"]))
     B, L, D = c["B"], c["L"], c["D"]
     flags = rn.RN_RMS if c["norm"] == "rms" else 0
     flags |= rn.RN_WEIGHT if "weight" in c else 0
     flags |= rn.RN_BIAS if "bias" in c else 0
-    d = {k: to_dev(c[k], dev) for k in ("x", "residual", "gate", "weight", "bias", "scale", "shift")
-         if k in c}
-    y = torch.full((B * L * D,), float("nan"), dtype=torch.bfloat16, device=dev)
+    d = {k: to_dev(c[k], dev) for k in ("x", "residual", "gate", "scale", "shift") if k in c}
+    for k in ("weight", "bias"):
+        if k in c:
+            d[k] = torch.from_numpy(c[k]).to(dev) if c["affine"] == "f32" else to_dev(c[k], dev)
+    aff = rn.RN_DTYPE_F32 if c["affine"] == "f32" else rn.RN_DTYPE_BF16
+    ydt = {"bf16": (rn.RN_DTYPE_BF16, torch.bfloat16), "f32": (rn.RN_DTYPE_F32, torch.float32),
+           "fp8": (rn.RN_DTYPE_FP8_E4M3, torch.float8_e4m3fn)}[c["out"]]
+    y = torch.zeros((B * L * D,), dtype=ydt[1], device=dev)
+    ys = torch.zeros((B * L,), dtype=torch.float32, device=dev) if c["out"] == "fp8" else None
     if c["op"] == "fused":
         flags |= rn.RN_GATE
-        ro = torch.full_like(y, float("nan"))
-        rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d["gate"], d.get("weight"),
-                             d.get("bias"), d["scale"], d["shift"], B, L, D, flags,
-                             c["layout.gate"], c["layout.ss"], c["eps"])
+        ro = torch.full((B * L * D,), float("nan"), dtype=torch.bfloat16, device=dev)
+        rn.resnorm_fused_fwd_ex(y, ro, d["x"], d["residual"], d["gate"], d.get("weight"),
+                                d.get("bias"), d["scale"], d["shift"], B, L, D, flags,
+                                c["layout.gate"], c["layout.ss"], c["eps"], aff, ydt[0], ys)
     else:
-        rn.norm_scale_shift_fwd(y, d["x"], d.get("weight"), d.get("bias"), d["scale"],
-                                d["shift"], B, L, D, flags, c["layout.ss"], c["eps"])
+        rn.norm_scale_shift_fwd_ex(y, d["x"], d.get("weight"), d.get("bias"), d["scale"],
+                                   d["shift"], B, L, D, flags, c["layout.ss"], c["eps"], aff, ydt[0], ys)
     torch.cuda.synchronize()
     if c["op"] == "fused":
         np.testing.assert_array_equal(to_host(ro), c["expect.residual_out"])
-    got = to_host(y)
-    ok, max_ulps, n_bad, first = check_y(got, c["expect.y"])
-    assert ok, "%s: y[%d] = %r, expected %r" % (c["name"], first, bf16_to_f64(got[first]),
-                                                bf16_to_f64(c["expect.y"][first]))
+    if c["out"] == "bf16":
+        got = to_host(y)
+        ok, max_ulps, n_bad, first = check_y(got, c["expect.y"])
+        assert ok, "%s: y[%d] = %r, expected %r" % (c["name"], first, bf16_to_f64(got[first]),
+                                                    bf16_to_f64(c["expect.y"][first]))
+    elif c["out"] == "f32":
+        got = y.cpu().numpy().astype(np.float64)
+        ref = c["expect.y"].astype(np.float64)
+        assert np.all(np.abs(got - ref) <= 2.0 ** -14 * np.maximum(1.0, np.abs(ref))), (got, ref)
+    else:
+        codes = y.view(torch.uint8).cpu().numpy()
+        np.testing.assert_allclose(ys.cpu().numpy(), c["expect.y_scale"], rtol=2.0 ** -20, atol=0)
+        np.testing.assert_array_equal(codes, c["expect.y"])
