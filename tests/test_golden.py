@@ -24,7 +24,7 @@ def _op_rows(lay, B, L):
 def test_fixture_is_consistent():
     """Sizes in every case agree with its layouts, so a bad fixture cannot pass
     silently."""
-    assert len(CASES) == 11
+    assert len(CASES) == 12
     for c in CASES:
         B, L, D = c["B"], c["L"], c["D"]
         n = B * L * D
@@ -92,6 +92,8 @@ def test_hip_path_reproduces_worked_rows(case):
         np.testing.assert_array_equal(to_host(ro), c["expect.residual_out"])
     if c["out"] == "bf16":
         got = to_host(y)
+        if c.get("gpu") == "exact":
+            np.testing.assert_array_equal(got, c["expect.y"])
         ok, max_ulps, n_bad, first = check_y(got, c["expect.y"])
         assert ok, "%s: y[%d] = %r, expected %r" % (c["name"], first, bf16_to_f64(got[first]),
                                                     bf16_to_f64(c["expect.y"][first]))
