@@ -109,6 +109,16 @@ __device__ __forceinline__ void store16(u32x4 v, __amdgpu_buffer_rsrc_t r, uint3
   pace<PACE>();
 }
 
+// s_waitcnt on vmcnt alone (expcnt and lgkmcnt at their maxima, i.e. not
+// waited for): the gfx9 encoding keeps vmcnt bits 3:0 in bits 3:0 of the
+// immediate and bits 5:4 in bits 15:14.
+constexpr int kVmcntMax = 63;
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N <= kVmcntMax, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // bf16 pair <-> fp32: the low half of a dword is the element at the lower
 // address.  Widening is a shift; narrowing is one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
@@ -308,9 +318,18 @@ void row_kernel(const RowArgs a) {
   constexpr int PL = kPaceLoads;
   constexpr int PS = OP::out == kOutF32 ? kPaceStoresF32 : kPaceStores;
   static_assert(W * RPB * kWaveSize <= 1024, "workgroup size");
-  [[maybe_unused]] __shared__ float red_sum[W * RPB];
-  [[maybe_unused]] __shared__ float red_sq[W * RPB];
-  [[maybe_unused]] __shared__ float red_max[W * RPB];
+  // Cross-wave partials.  With several rows per slot (K > 1) and several
+  // waves per row, one barrier per row does not keep a wave that has moved
+  // on to row k + 1 from overwriting its row-k partial before a slower wave
+  // of the row has read it (RMSNorm has a single barrier per row).  Rows
+  // alternate between two copies by parity: row k + 2 writes copy k & 1
+  // only after the barrier of row k + 1, which every wave reaches after
+  // its reads of row k.
+  constexpr int NBUF = (K > 1 && W > 1) ? 2 : 1;
+  constexpr int NRED = W * RPB;
+  [[maybe_unused]] __shared__ float red_sum_buf[NBUF * NRED];
+  [[maybe_unused]] __shared__ float red_sq_buf[NBUF * NRED];
+  [[maybe_unused]] __shared__ float red_max_buf[NBUF * NRED];
 
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t lane = threadIdx.x & (kWaveSize - 1);
@@ -409,7 +428,10 @@ void row_kernel(const RowArgs a) {
     else load_ss(std::integral_constant<int, kPolicyDefault>{});
   };
   // ---- the rest of a row, once its loads are issued ----
-  auto process = [&](const RowPos& p) __attribute__((always_inline)) {
+  auto process = [&](const RowPos& p, uint32_t copy) __attribute__((always_inline)) {
+    float* const red_sum = red_sum_buf + copy * NRED;
+    float* const red_sq = red_sq_buf + copy * NRED;
+    float* const red_max = red_max_buf + copy * NRED;
     // ---- residual update (fused) ----
     if constexpr (OP::fused) {
       const auto rs_ro = row_rsrc((const char*)a.residual_out + p.off, p.bytes);
@@ -670,10 +692,18 @@ void row_kernel(const RowArgs a) {
       load_rows(p0);
     }
     if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
-    // the LDS fill complete in every wave (the compiler waits for the loads
-    // first; no store has been issued yet, so only loads are waited for)
-    if constexpr (kLds) __syncthreads();
-    process(p0);
+    if constexpr (kLds) {
+      // Every wave's LDS fill must have landed before any wave reads LDS.
+      // The fills were issued first and vmcnt counts loads in issue order,
+      // so waiting until no more than the loads issued after them (gate,
+      // scale/shift, x, residual) are outstanding covers exactly the fills
+      // and leaves the row's own loads in flight.  No store has been issued
+      // yet.  The barrier then makes every wave's fill visible to all.
+      constexpr int kAfterFills = (OP::gate ? VPT : 0) + 2 * VPT + 2 * VPT;
+      vmcnt_wait<(kAfterFills < kVmcntMax ? kAfterFills : kVmcntMax)>();
+      __syncthreads();
+    }
+    process(p0, 0);
   } else {
     // K consecutive rows share the slot's modulation rows and the affine
     // rows: those are loaded once, then each row streams its own operands
@@ -692,7 +722,7 @@ void row_kernel(const RowArgs a) {
       if constexpr (W == 1) __builtin_amdgcn_s_setprio(3);
       load_rows(p);
       if constexpr (W == 1) __builtin_amdgcn_s_setprio(0);
-      process(p);
+      process(p, (uint32_t)(k & (NBUF - 1)));
     }
   }
 }

@@ -126,6 +126,15 @@ def test_fused_affine_stages_weight_in_lds(fused_asm, aff, lds_loads, lds_reads,
     assert _count(body, "ds_read_b128") == lds_reads
     assert not re.search(r"^\s+ds_(?!read_b128)", body, re.M)   # nothing else touches LDS
     assert _count(body, "s_barrier") == 1
+    # The fills complete before the barrier: the last wait ahead of it allows
+    # at most the 50 loads issued after the fills (gate, scale/shift, x,
+    # residual; 10 vectors each) to be outstanding, and no fill follows it.
+    lines = body.splitlines()
+    bar = next(i for i, ln in enumerate(lines) if re.match(r"\s+s_barrier\b", ln))
+    wait = next(i for i in range(bar - 1, -1, -1)
+                if re.match(r"\s+s_waitcnt\b.*\bvmcnt\(", lines[i]))
+    assert int(re.search(r"vmcnt\((\d+)\)", lines[wait]).group(1)) <= 50
+    assert not any(re.search(r"buffer_load.*\blds\b", ln) for ln in lines[wait:bar])
     assert _count(body, "buffer_store_dwordx4") == 20
     assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == lds_bytes
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
@@ -152,3 +161,37 @@ def test_multi_row_kernel_loads_shared_rows_once(nss_asm, shape, w, vpt):
     assert (_count(body, "s_barrier") > 0) == (w > 1)
     assert _meta_int(meta, "amdhsa_private_segment_fixed_size") == 0
     assert _meta_int(meta, "vgpr_count") <= 256 and not _meta_int(meta, "agpr_count")
+
+
+@pytest.fixture(scope="module")
+def nss_rms_asm(tmp_path_factory):
+    return _asm("rn_inst_nss_rms_bf16.hip", tmp_path_factory.mktemp("asm_nss_rms"))
+
+
+@pytest.mark.parametrize("shape,w,rpb,vpt", [(29, 2, 2, 3), (30, 2, 2, 4), (31, 2, 2, 5),
+                                             (32, 4, 1, 3), (33, 4, 1, 4), (34, 4, 1, 5)])
+@pytest.mark.parametrize("aff", [1, 4])
+def test_multi_row_rms_partials_alternate_copies(nss_rms_asm, shape, w, rpb, vpt, aff):
+    """RMSNorm has one barrier per row, so on the multi-row shapes with several
+    waves per row consecutive rows must write their cross-wave partials to
+    different LDS copies (a wave that moves on to the next row must not
+    overwrite a partial a slower wave of the row has yet to read): the first
+    LDS write of each of the 4 rows alternates between two offsets, and the
+    workgroup's LDS holds two copies of the sum-of-squares and maximum
+    partials."""
+    sym = "_ZN2rn10row_kernelINS_2OpILb1ELb0ELb0ELi%dELi0EEELi%dEEEvNS_7RowArgsE" % (aff, shape)
+    body, meta = _kernel(nss_rms_asm, sym)
+    lines = body.splitlines()
+    stores = [i for i, ln in enumerate(lines) if re.match(r"\s+buffer_store_dwordx4\b", ln)]
+    assert len(stores) == 4 * vpt
+    ends = [stores[vpt * k + vpt - 1] for k in range(4)]
+    starts = [0] + [e + 1 for e in ends[:-1]]
+    offs = []
+    for a, b in zip(starts, ends):
+        first = next(ln for ln in lines[a:b] if re.match(r"\s+ds_write_b32\b", ln))
+        m = re.search(r"offset:(\d+)", first)
+        offs.append(int(m.group(1)) if m else 0)
+    assert all(offs[k] != offs[k + 1] for k in range(3)), offs
+    assert offs[0] == offs[2] and offs[1] == offs[3], offs
+    nred = w * rpb
+    assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == 2 * 2 * nred * 4
