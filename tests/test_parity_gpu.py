@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import (compare_outputs, launch_workload, log, require_gpu, to_dev, to_host,
-                      workload_flags)
+from gpu_util import (FULL_SIZE_MIN_IDENTICAL, compare_outputs, launch_workload, log,
+                      require_gpu, to_dev, to_host, workload_flags)
 from util import bf16_to_f64
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,7 @@ def orc():
     return oracle.Oracle()
 
 
-def _run_full(rn, orc, wl, check_rows=None):
+def _run_full(rn, orc, wl, check_rows=None, min_identical=None):
     import torch
     log("workload %s: generating inputs" % wl.name)
     inp = synth.make_inputs(wl, threads=THREADS)
@@ -50,24 +50,28 @@ def _run_full(rn, orc, wl, check_rows=None):
     del d, y, ro
     log("workload %s: oracle on %d rows x %d threads" % (wl.name, wl.R, THREADS))
     y_ref, ro_ref, _ = orc.run_workload(wl, inp, threads=THREADS)
-    st = compare_outputs(yh, y_ref, roh, ro_ref, wl.name)
+    st = compare_outputs(yh, y_ref, roh, ro_ref, wl.name, min_identical=min_identical)
     log("workload %s: OK  %sy: max %.0f ulp where |y|>=1, max %.0f ulp where "
         "|y|>=2^-6, max abs err %.3g, %.5f%% bit-identical"
         % (wl.name, "residual_out bit-exact; " if roh is not None else "", st["ulp_ge1"], st["ulp_ge_1_64"], st["abs"], 100 * st["identical"]))
     return inp, yh, roh
 
 
-@pytest.mark.parametrize("name", ["fused_ln_b1_l16_d5120", "fused_rms_w_b2_l16_d10240"])
+@pytest.mark.parametrize("name", ["fused_ln_b1_l16_d5120", "fused_rms_w_b2_l16_d10240",
+                                  "fused_ln_b2_l16_d5120", "nss_ln_b1_l16_d5120",
+                                  "nss_ln_b2_l16_d5120"])
 def test_small_workloads_all_rows(rn, orc, name):
     _run_full(rn, orc, synth.WORKLOADS[name])
 
 
 @pytest.mark.parametrize("name", ["fused_ln_b1_l90000_d5120", "fused_rms_w_b1_l90000_d10240",
-                                  "nss_ln_b1_l176400_d5120", "fused_ln_frame_b1_f49_l176400_d5120"])
+                                  "nss_ln_b1_l176400_d5120", "fused_ln_frame_b1_f49_l176400_d5120",
+                                  "nss_ln_b1_l90000_d5120"])
 def test_full_size_workloads_all_rows(rn, orc, name):
     """Every row of the full-size workloads, in the launch configuration the
-    benchmark times, against the oracle."""
-    _run_full(rn, orc, synth.WORKLOADS[name])
+    benchmark times, against the oracle; at most 0.05 % of y may differ in
+    any bit."""
+    _run_full(rn, orc, synth.WORKLOADS[name], min_identical=FULL_SIZE_MIN_IDENTICAL)
 
 
 def _small_problem(seed, fused, rms, gate_layout, aff, ss_layout, B, L, D):
