@@ -22,6 +22,12 @@
  *   - Arguments are validated on the host before anything is enqueued.  On a
  *     non-OK status nothing was enqueued and rn_last_error() describes the
  *     problem.  There is no fallback path: an unsupported case is an error.
+ *     (The pages' history is of silent fallbacks: an unavailable fused kernel
+ *     quietly replaced by the native path -- sglang PR #36349, "Motivation";
+ *     sglang PR #33144, "Motivation".)
+ *   - The host keeps, per thread, the last call it validated with its launch
+ *     plan: a call that repeats it exactly (same pointers, sizes, flags,
+ *     layouts, eps and element types) is enqueued without validating again.
  *   - B * L == 0 is valid and enqueues nothing.
  *   - Exact aliasing y == x and residual_out == residual is allowed (each
  *     element is read before it is overwritten, by the same thread); any other
@@ -112,6 +118,7 @@ typedef struct {
  *   y, residual_out  [B*L, D] outputs (y may be x; residual_out may be residual)
  *   x, residual      [B*L, D] inputs
  *   gate             rows per gate_layout; must be NULL iff !(flags & RN_GATE)
+ *                    (without RN_GATE, gate_layout is ignored)
  *   weight, bias     [D]; NULL iff the corresponding flag is clear
  *   scale, shift     rows per ss_layout; required
  *   B, L, D          B, L >= 0; 8 <= D <= RN_D_MAX, D % 8 == 0
@@ -170,7 +177,11 @@ rn_status norm_scale_shift_fwd_ex(void* y, const void* x, const void* weight, co
                                   const rn_ext* ext, void* stream);
 
 /* Text describing the last non-OK status returned on the calling thread
- * (empty if none).  The pointer stays valid until the thread's next call. */
+ * (empty if none).  The pointer stays valid until the thread's next call.
+ * Every refusal carries its reason, because the failure this library is
+ * built against is the silent one: the pages describe fused kernels that
+ * fell back to the native path without a word (sglang PR #36349,
+ * "Motivation"; sglang PR #33144, "Motivation"). */
 const char* rn_last_error(void);
 
 /* Launch shape the library would use for a problem (host-only query; no

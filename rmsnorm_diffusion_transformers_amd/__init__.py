@@ -15,6 +15,8 @@ Low level (same names and argument order as the C entry points):
                          ss_layout, eps, stream)
     resnorm_fused_fwd_ex / norm_scale_shift_fwd_ex: the same plus affine_dtype,
     y_dtype and y_scale (binary32 weight/bias; binary32 or FP8 E4M3 y)
+    prepare(entry, *args): check a call once; returns a callable that
+    enqueues it again (for loops over the same buffers)
 Tensor level (operand order of the custom ops flydsl_fused_residual_norm_scale_shift
 and flydsl_norm_scale_shift, sglang PR #36349, "Microbenchmark"):
     fused_residual_norm_scale_shift(residual, x, gate, weight, bias, scale, shift,
@@ -203,6 +205,30 @@ def _layout(lay) -> rn_layout:
     return rn_layout(int(kind), int(frames))
 
 
+def _args_fused(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D, flags,
+                gate_layout, ss_layout, eps, stream, affine_dtype, y_dtype, y_scale):
+    """Checked C arguments of resnorm_fused_fwd_ex."""
+    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                        gate_layout, ss_layout, y_scale)
+    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    return (_lib.resnorm_fused_fwd_ex,
+            (_addr(y, y_dtype), _addr(residual_out), _addr(x), _addr(residual), _addr(gate),
+             _addr(weight, affine_dtype), _addr(bias, affine_dtype), _addr(scale), _addr(shift),
+             int(B), int(L), int(D), int(flags), _layout(gate_layout), _layout(ss_layout),
+             float(eps), ctypes.byref(ext), _stream(stream, dev)), ext)
+
+
+def _args_nss(y, x, weight, bias, scale, shift, B, L, D, flags, ss_layout, eps, stream,
+              affine_dtype, y_dtype, y_scale):
+    """Checked C arguments of norm_scale_shift_fwd_ex."""
+    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale)
+    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    return (_lib.norm_scale_shift_fwd_ex,
+            (_addr(y, y_dtype), _addr(x), _addr(weight, affine_dtype), _addr(bias, affine_dtype),
+             _addr(scale), _addr(shift), int(B), int(L), int(D), int(flags), _layout(ss_layout),
+             float(eps), ctypes.byref(ext), _stream(stream, dev)), ext)
+
+
 def resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
                       flags, gate_layout=(RN_BCAST, 0), ss_layout=(RN_BCAST, 0), eps=1e-6,
                       stream=None) -> None:
@@ -250,15 +276,10 @@ def resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale
     """Enqueue the fused op with other element types (C entry point of the same
     name): binary32 weight/bias; binary32 or FP8 E4M3 y (FP8 with per-row
     binary32 scales in y_scale)."""
-    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
-                        gate_layout, ss_layout, y_scale)
-    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
-    _check(_lib.resnorm_fused_fwd_ex(_addr(y, y_dtype), _addr(residual_out), _addr(x),
-                                     _addr(residual), _addr(gate),
-                                     _addr(weight, affine_dtype), _addr(bias, affine_dtype),
-                                     _addr(scale), _addr(shift), int(B), int(L), int(D),
-                                     int(flags), _layout(gate_layout), _layout(ss_layout),
-                                     float(eps), ctypes.byref(ext), _stream(stream, dev)))
+    fn, args, _ext = _args_fused(y, residual_out, x, residual, gate, weight, bias, scale, shift,
+                                 B, L, D, flags, gate_layout, ss_layout, eps, stream, affine_dtype,
+                                 y_dtype, y_scale)
+    _check(fn(*args))
 
 
 def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
@@ -266,12 +287,47 @@ def norm_scale_shift_fwd_ex(y, x, weight, bias, scale, shift, B, L, D, flags,
                             y_dtype=RN_DTYPE_BF16, y_scale=None, stream=None) -> None:
     """Enqueue the norm-only op with other element types (C entry point of the
     same name)."""
-    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale)
-    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
-    _check(_lib.norm_scale_shift_fwd_ex(_addr(y, y_dtype), _addr(x), _addr(weight, affine_dtype),
-                                        _addr(bias, affine_dtype), _addr(scale), _addr(shift),
-                                        int(B), int(L), int(D), int(flags), _layout(ss_layout),
-                                        float(eps), ctypes.byref(ext), _stream(stream, dev)))
+    fn, args, _ext = _args_nss(y, x, weight, bias, scale, shift, B, L, D, flags, ss_layout, eps,
+                               stream, affine_dtype, y_dtype, y_scale)
+    _check(fn(*args))
+
+
+def prepare(entry, *args, **kwargs):
+    """Check a call once and return a callable that enqueues it again.
+
+    entry is resnorm_fused_fwd, norm_scale_shift_fwd or their _ex forms; the
+    other arguments are that entry point's.  Every host-side check runs here
+    once (tensor devices, sizes, element types, contiguity) and the stream is
+    bound now (torch's current stream of the operands' device unless one is
+    given); the returned callable only calls the C entry point with the
+    stored arguments and raises RnError on a non-OK status.  For loops that
+    call the op on the same buffers every step: the tensors must stay alive
+    and keep their storage while the callable is used.  The library keeps the
+    last validated problem of each thread, so repeating a call costs the
+    launch only."""
+    names = {resnorm_fused_fwd: ("fused", False), resnorm_fused_fwd_ex: ("fused", True),
+             norm_scale_shift_fwd: ("nss", False), norm_scale_shift_fwd_ex: ("nss", True)}
+    if entry not in names:
+        raise ValueError("prepare() takes resnorm_fused_fwd, norm_scale_shift_fwd or their _ex forms")
+    op, ex = names[entry]
+    import inspect
+    bound = inspect.signature(entry).bind(*args, **kwargs)
+    bound.apply_defaults()
+    a = dict(bound.arguments)
+    if not ex:
+        a.update(affine_dtype=RN_DTYPE_BF16, y_dtype=RN_DTYPE_BF16, y_scale=None)
+    if op == "fused":
+        fn, cargs, ext = _args_fused(**a)
+    else:
+        fn, cargs, ext = _args_nss(**a)
+    # ctypes objects built once; ext stays referenced by the closure
+    conv = tuple(t(v) if isinstance(v, (int, float)) else v for t, v in zip(fn.argtypes, cargs))
+
+    def launch(_fn=fn, _args=conv, _ext=ext):
+        st = _fn(*_args)
+        if st != RN_OK:
+            raise RnError(st, last_error())
+    return launch
 
 
 def describe_launch(B, L, D, flags, fused=True, gate_layout=(RN_BCAST, 0),
