@@ -32,9 +32,12 @@ reference; and the CPU oracle baseline.
 Prints ONE JSON line.  Options: --gpus N (only 1: this path is measured on one
 GPU), --steps K, --warmup W, --placement planned|default, --calibrate (time a
 plain elementwise copy, used to scale rocprof byte counters), --no-cpu-baseline,
---no-extras, --workload NAME, --placement-map (the granule class map of the
-headline kernel, one JSON line), --placement-widths (torch's allocations against
-a planned placement at row widths 2048-10240, one JSON line).
+--no-extras, --no-companion, --workload NAME, --placement-map (the granule class
+map of the headline kernel), --placement-thirds (its rate against the outputs'
+place in one large allocation at 512 MiB steps), --placement-counters (three
+placements, 40 launches each, for rocprofv3 counter runs), --placement-widths
+(torch's allocations against a planned placement at row widths 2048-10240);
+each of the placement modes prints one JSON line of its own.
 """
 from __future__ import annotations
 
@@ -56,7 +59,7 @@ HEADLINE = "fused_ln_frame_b1_f49_l176400_d5120"
 # other large workloads (fused LayerNorm at L 90000 with 1 % of rows scaled
 # by 50; fused RMSNorm + weight with per-row scale/shift at D 10240).
 COMPANIONS = ["nss_ln_b1_l176400_d5120", "fused_ln_b1_l90000_d5120",
-              "fused_rms_w_b1_l90000_d10240"]
+              "fused_rms_w_b1_l90000_d10240", "nss_ln_b1_l90000_d5120"]
 KERNEL_SOURCES = ["rmsnorm_diffusion_transformers_amd/csrc/rn_row_kernel.hpp",
                   "rmsnorm_diffusion_transformers_amd/csrc/rn_args.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
@@ -107,11 +110,48 @@ def upload(inp, dev):
             for k, v in inp.items()}
 
 
-def time_calls(fn, steps, warmup):
-    """Average ms per call of fn() over `steps` calls after `warmup`, timed
-    with events on the current stream (the stream the kernels run on)."""
+# Wall time the GPU is kept busy with the timed call itself before its warmup
+# steps.  Measured on MI355X: after a second without kernels (input
+# generation, host-to-device copies) the chip sits at idle clocks, and the
+# first ~15-30 launches of these kernels run 3-5 % slower until its clocks
+# and fabric have ramped (the fused headline's launches 1.256 -> 1.19 ms over
+# the first 20 ms; the norm-only op's 0.648 -> 0.601 ms).  A fixed number of
+# warmup launches covers that only for long runs; the settle phase covers it
+# whatever the step counts, and it changes nothing in the timed region.
+SETTLE_S = 0.1
+
+
+_settle_count = [0]
+
+
+def settle_launches():
+    """Calls made by the last settle()."""
+    return _settle_count[0]
+
+
+def settle(fn, seconds=SETTLE_S):
+    """Run fn() back to back, in batches that double up to 64 calls, until
+    `seconds` of wall time have passed; returns the number of calls."""
+    import torch
+    n, batch, t0 = 0, 1, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn()
+        n += batch
+        batch = min(2 * batch, 64)
+        torch.cuda.synchronize()
+    _settle_count[0] = n
+    return n
+
+
+def time_calls(fn, steps, warmup, settle_s=SETTLE_S):
+    """Average ms per call of fn() over `steps` calls after a settle phase
+    (settle()) and `warmup` calls, timed with events on the current stream
+    (the stream the kernels run on)."""
     import torch
     stream = torch.cuda.current_stream()
+    if settle_s > 0:
+        settle(fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -326,7 +366,7 @@ def extras(rn, dev_tensors, steps, warmup):
     ]
     out = []
     for name, what, fn, nbytes in cases:
-        ms, _ = time_calls(fn, max(10, steps // 4), max(3, warmup // 4))
+        ms, _ = time_calls(fn, steps, warmup)
         gbs = nbytes / (ms * 1e-3) / 1e9
         log("%s: %.4f ms/launch, %.1f GB/s" % (name, ms, gbs))
         out.append({"variant": name, "what": what, "ms_per_launch": round(ms, 5),
@@ -342,7 +382,7 @@ def extras(rn, dev_tensors, steps, warmup):
             fused_bcast()
         nss_bcast()
 
-    fwd_ms, _ = time_calls(forward, 3, 1)
+    fwd_ms, _ = time_calls(forward, 3, 1, settle_s=0)   # right after the variants: warm
     log("DiT forward mix: %.2f ms per forward (121 calls)" % fwd_ms)
     mix = {"ms_per_forward": round(fwd_ms, 3),
            "calls": {"norm_scale_shift (no affine)": 41, "fused, fp32 affine": 40,
@@ -361,6 +401,18 @@ def flags_of(rn, wl):
     return f
 
 
+def prepare_workload(rn, wl, d, y, ro, stream):
+    """launch_workload's call, checked once (rn.prepare)."""
+    flags = flags_of(rn, wl)
+    if wl.op == "fused":
+        return rn.prepare(rn.resnorm_fused_fwd, y, ro, d["x"], d["residual"], d.get("gate"),
+                          d.get("weight"), d.get("bias"), d["scale"], d["shift"], wl.B, wl.L,
+                          wl.D, flags, wl.gate_layout or (0, 0), wl.ss_layout, wl.eps, stream)
+    return rn.prepare(rn.norm_scale_shift_fwd, y, d["x"], d.get("weight"), d.get("bias"),
+                      d["scale"], d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps,
+                      stream)
+
+
 def launch_workload(rn, wl, d, y, ro, stream):
     """One pass of the workload through the C entry points."""
     flags = flags_of(rn, wl)
@@ -373,10 +425,17 @@ def launch_workload(rn, wl, d, y, ro, stream):
                                 d["shift"], wl.B, wl.L, wl.D, flags, wl.ss_layout, wl.eps, stream)
 
 
-def small_batch_latency(rn, dev, names=("fused_ln_b1_l16_d5120", "fused_rms_w_b2_l16_d10240")):
-    """The L = 16 workloads are launch- and latency-bound (their bytes fit in
-    cache): per-call time of back-to-back launches on the stream, and with 100
-    launches captured in one HIP graph and replayed (wall time / 100)."""
+SMALL = ("fused_ln_b1_l16_d5120", "fused_ln_b2_l16_d5120", "nss_ln_b1_l16_d5120",
+         "nss_ln_b2_l16_d5120", "fused_rms_w_b2_l16_d10240")
+
+
+def small_batch_latency(rn, dev, names=SMALL):
+    """The L = 16 workloads (the pages' speed matrix at B 1 and 2, D 5120, and
+    the RMS case at D 10240) are launch- and latency-bound (their bytes fit
+    in cache): per-call time of back-to-back launches on the stream through
+    the checked binding and through a prepared call (rn.prepare: the checks
+    done once), and with 100 launches captured in one HIP graph and replayed
+    (wall time / 100)."""
     import torch
 
     import synth
@@ -385,9 +444,11 @@ def small_batch_latency(rn, dev, names=("fused_ln_b1_l16_d5120", "fused_rms_w_b2
         wl = synth.WORKLOADS[name]
         d = upload(synth.make_inputs(wl, threads=1), dev)
         y = torch.empty_like(d["x"])
-        ro = torch.empty_like(d["x"])
+        ro = torch.empty_like(d["x"]) if wl.op == "fused" else None
         stream = torch.cuda.current_stream()
         eager_ms, _ = time_calls(lambda: launch_workload(rn, wl, d, y, ro, stream), 200, 20)
+        prepared = prepare_workload(rn, wl, d, y, ro, stream)
+        prep_ms, _ = time_calls(prepared, 200, 20)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -400,10 +461,11 @@ def small_batch_latency(rn, dev, names=("fused_ln_b1_l16_d5120", "fused_rms_w_b2
                 launch_workload(rn, wl, d, y, ro, torch.cuda.current_stream())
         graph_ms, _ = time_calls(g.replay, 20, 3)
         out.append({"workload": name, "us_per_call_stream": round(eager_ms * 1e3, 2),
+                    "us_per_call_prepared": round(prep_ms * 1e3, 2),
                     "us_per_call_graph": round(graph_ms * 1e3 / 100, 2),
                     "algorithmic_bytes": wl.algorithmic_bytes()})
-        log("%s: %.2f us/call on the stream, %.2f us/call in a graph" % (
-            name, eager_ms * 1e3, graph_ms * 1e3 / 100))
+        log("%s: %.2f us/call on the stream (%.2f prepared), %.2f us/call in a graph" % (
+            name, eager_ms * 1e3, prep_ms * 1e3, graph_ms * 1e3 / 100))
         del g, d, y, ro
     # the floor: a one-element torch.neg, 100 launches captured and replayed the same way
     a = torch.zeros(1, device=dev)
@@ -479,7 +541,7 @@ def placement_map(rn, dev, granules=7):
 
     def rate(x, r, y, o, steps=16):
         call = lambda: launch_workload(rn, wl, dict(small, x=x, residual=r), y, o, stream)  # noqa: E731
-        ms, _ = time_calls(call, steps, 3)
+        ms, _ = time_calls(call, steps, 3, settle_s=0)   # back to back with the other trials
         return wl.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
 
     ref_place = (0, 0, 1, 2)
@@ -528,6 +590,113 @@ def placement_map(rn, dev, granules=7):
     print(json.dumps(out), flush=True)
 
 
+def _headline_on(rn, dev):
+    """(inputs, small device operands, launch factory) of the headline workload:
+    the factory takes (x, residual, y, residual_out) views."""
+    import torch
+
+    import synth
+    wl = synth.WORKLOADS[HEADLINE]
+    inp = make_inputs(wl)
+    small = upload({k: inp[k] for k in ("gate", "scale", "shift")}, dev)
+    stream = torch.cuda.current_stream()
+
+    def make(x, r, y, o):
+        return lambda: launch_workload(rn, wl, dict(small, x=x, residual=r), y, o, stream)
+    return wl, inp, make
+
+
+def placement_thirds(rn, dev, step_gib=0.5):
+    """The headline kernel's rate against where its outputs sit in one large
+    allocation: x and residual at its start; an adjacent output pair
+    (residual_out at P, y at P + 2 GiB) swept over the allocation; then y
+    swept over it with residual_out fixed at 40 GiB and at 100.5 GiB.  Steps
+    of `step_gib`; 10 launches after 2 for each point.  Prints one JSON line."""
+    import torch
+
+    from rmsnorm_diffusion_transformers_amd import hbm
+    GiB = 1 << 30
+    wl, inp, make = _headline_on(rn, dev)
+    R, D = wl.R, wl.D
+
+    def frac(call):
+        ms, _ = time_calls(call, 10, 2, settle_s=0)
+        return round(wl.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+
+    arena = hbm.HbmArena(dev)
+    N = arena.nbytes
+    view = lambda off: arena.view(int(off), (R, D), torch.bfloat16)  # noqa: E731
+    x, r = view(0), view(2 * GiB)
+    x.copy_(host_bf16(inp["x"]))
+    r.copy_(host_bf16(inp["residual"]))
+    del inp
+    settle(make(x, r, view(4 * GiB), view(6 * GiB)), 0.2)
+    step = int(step_gib * GiB)
+    out = {"workload": wl.name, "allocation_gib": N / GiB, "step_gib": step_gib,
+           "device_memory_gib": round(torch.cuda.get_device_properties(dev).total_memory / GiB, 3)}
+    adj, P = [], 4 * GiB
+    while P + 4 * GiB <= N:
+        adj.append([P / GiB, frac(make(x, r, view(P + 2 * GiB), view(P)))])
+        P += step
+    out["adjacent_pair"] = adj
+    for anchor in (40 * GiB, 100 * GiB + GiB // 2):
+        if anchor + 2 * GiB > N:
+            continue
+        sw, P = [], 4 * GiB
+        while P + 2 * GiB <= N:
+            if abs(P - anchor) >= 2 * GiB:
+                sw.append([P / GiB, frac(make(x, r, view(P), view(anchor)))])
+            P += step
+        out["y_sweep_residual_out_at_%g" % (anchor / GiB)] = sw
+    log("placement thirds: %d + sweep points" % len(adj))
+    del x, r
+    arena.release()
+    print(json.dumps(out), flush=True)
+
+
+def placement_counters(rn, dev, n=40):
+    """The headline kernel on three placements, n launches each, in this order:
+    torch's back-to-back allocations; one large allocation with both outputs in
+    its first third (residual_out at 40 GiB, y at 60 GiB); the same with the
+    outputs in two thirds (y at 150 GiB).  A counter trace of this command
+    splits by dispatch index (0..n-1, n..2n-1, 2n..3n-1); without a profiler
+    the printed line gives each placement's rate from its n launches."""
+    import torch
+
+    from rmsnorm_diffusion_transformers_amd import hbm
+    GiB = 1 << 30
+    wl, inp, make = _headline_on(rn, dev)
+    R, D = wl.R, wl.D
+    res = {}
+
+    def run(name, call):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(n):
+            call()
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / n
+        res[name] = round(wl.algorithmic_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        log("placement counters: %s %.4f ms" % (name, ms))
+
+    x, r = upload({"x": inp["x"]}, dev)["x"], upload({"r": inp["residual"]}, dev)["r"]
+    y, o = torch.empty_like(x), torch.empty_like(x)
+    run("torch_allocations", make(x, r, y, o))
+    del x, r, y, o
+    torch.cuda.empty_cache()
+    arena = hbm.HbmArena(dev)
+    view = lambda off: arena.view(int(off), (R, D), torch.bfloat16)  # noqa: E731
+    x, r = view(0), view(2 * GiB)
+    x.copy_(host_bf16(inp["x"]))
+    r.copy_(host_bf16(inp["residual"]))
+    run("outputs_in_one_third", make(x, r, view(60 * GiB), view(40 * GiB)))
+    run("outputs_in_two_thirds", make(x, r, view(150 * GiB), view(40 * GiB)))
+    del x, r
+    arena.release()
+    print(json.dumps({"workload": wl.name, "launches_each": n, "frac": res}), flush=True)
+
+
 def placement_widths(rn, dev, widths=(2048, 3072, 4096, 5120, 6144, 8192, 10240)):
     """Fused LayerNorm (broadcast gate/scale/shift) and the norm-only op at
     several row widths, 176400 x 5120 elements each: torch's own allocations
@@ -557,7 +726,7 @@ def placement_widths(rn, dev, widths=(2048, 3072, 4096, 5120, 6144, 8192, 10240)
             y, x, None, None, sc, sh, 1, L, D, 0, (0, 0), 1e-6, stream))
 
     def frac(nbytes, call):
-        ms, _ = time_calls(call, 40, 8)
+        ms, _ = time_calls(call, 40, 8, settle_s=0.05)
         return round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
 
     rows = {}
@@ -664,6 +833,12 @@ def main():
     ap.add_argument("--placement-map", action="store_true",
                     help="time the headline kernel on every assignment of its four streamed "
                          "tensors to distinct HBM granules and print the class map")
+    ap.add_argument("--placement-thirds", action="store_true",
+                    help="the headline kernel's rate against where its outputs sit in one large "
+                         "allocation, at 512 MiB steps")
+    ap.add_argument("--placement-counters", action="store_true",
+                    help="the headline kernel on three placements, 40 launches each, for a "
+                         "rocprofv3 counter run")
     ap.add_argument("--placement-widths", action="store_true",
                     help="torch's allocations against a planned placement for the fused and "
                          "norm-only ops at several row widths")
@@ -692,6 +867,12 @@ def main():
     if args.placement_widths:
         placement_widths(rn, dev)
         return
+    if args.placement_thirds:
+        placement_thirds(rn, dev)
+        return
+    if args.placement_counters:
+        placement_counters(rn, dev)
+        return
     wl = synth.WORKLOADS[args.workload]
     want_extras = not args.no_extras and args.workload == HEADLINE
     companions_wanted = not args.no_companion and args.workload == HEADLINE
@@ -699,21 +880,29 @@ def main():
     inp = make_inputs(wl)
     extra_out = [((wl.R, wl.D), torch.float32), ((wl.R, wl.D), torch.float8_e4m3fn)] if want_extras else []
 
-    # Row-kernel launches before the timed workloads (the default-allocation
-    # pass and the placement trials), so that a kernel trace can be split.
+    # Row-kernel launches before the timed workloads (the torch-allocation
+    # passes and the placement trials), so that a kernel trace can be split.
     prelude = 0
     placement = {"kind": "default"}
     arena = None
     plans = {}
     comp_inputs = {}
+    torch_alloc = {}
+    if companions_wanted:
+        for name in COMPANIONS:
+            comp_inputs[name] = make_inputs(synth.WORKLOADS[name])
     if args.placement == "planned":
-        # what torch's own allocations give on a fresh device, measured first
-        dms, _, _ = time_workload(rn, wl, args.steps, args.warmup, dev, inp=inp)
-        prelude += args.steps + args.warmup
-        dg = nbytes / (dms * 1e-3) / 1e9
-        log("%s, torch allocations: %.4f ms/launch, %.1f GB/s" % (wl.name, dms, dg))
-        placement["default_allocation"] = {"ms_per_launch": round(dms, 5), "GB/s": round(dg, 1),
-                                           "frac": round(dg / HBM_PEAK_GBS, 4)}
+        # what torch's own back-to-back allocations give, for every large
+        # workload, measured first (each workload's tensors freed after it)
+        for name, winp in [(wl.name, inp)] + list(comp_inputs.items()):
+            w = synth.WORKLOADS[name]
+            dms, _, _ = time_workload(rn, w, args.steps, args.warmup, dev, inp=winp)
+            prelude += settle_launches() + args.steps + args.warmup
+            dg = w.algorithmic_bytes() / (dms * 1e-3) / 1e9
+            log("%s, torch allocations: %.4f ms/launch, %.1f GB/s" % (name, dms, dg))
+            torch_alloc[name] = {"ms_per_launch": round(dms, 5), "GB/s": round(dg, 1),
+                                 "frac": round(dg / HBM_PEAK_GBS, 4)}
+        placement["default_allocation"] = torch_alloc[wl.name]
         try:
             arena = hbm.HbmArena(dev)
             if arena.granules < 3:
@@ -734,15 +923,12 @@ def main():
         except ValueError as e:
             log("%s: no placement (%s); torch allocations are used" % (wl.name, e))
             placement["note"] = str(e)
-        if companions_wanted:
-            for name in COMPANIONS:
-                wc = synth.WORKLOADS[name]
-                comp_inputs[name] = make_inputs(wc)
-                try:
-                    plans[name], _ = plan_workload(rn, wc, comp_inputs[name], arena, dev)
-                    prelude += hbm.launches(plans[name].candidates)
-                except ValueError as e:
-                    log("%s: no placement (%s); torch allocations are used" % (name, e))
+        for name, cinp in comp_inputs.items():
+            try:
+                plans[name], _ = plan_workload(rn, synth.WORKLOADS[name], cinp, arena, dev)
+                prelude += hbm.launches(plans[name].candidates)
+            except ValueError as e:
+                log("%s: no placement (%s); torch allocations are used" % (name, e))
     log("row-kernel launches before the timed workloads: %d" % prelude)
 
     pl = plans.get(wl.name)
@@ -784,6 +970,8 @@ def main():
                      "launch": ci}
             if name in plans:
                 entry["placement"] = plans[name].describe()
+            if name in torch_alloc:
+                entry["torch_allocation"] = torch_alloc[name]
             companions.append(entry)
     if arena is not None:
         arena.release()
@@ -811,7 +999,11 @@ def main():
                    "gate_layout": wl.gate_layout, "ss_layout": wl.ss_layout,
                    "algorithmic_bytes": nbytes, "launch": info},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name)},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
+                     "frac_torch_allocation": torch_alloc.get(wl.name, {}).get("frac")},
+        # the same kernel and workload on torch's own back-to-back allocations
+        # (x, residual, y, residual_out allocated one after the other)
+        "torch_allocation": torch_alloc.get(wl.name),
         "placement": placement,
         "wall_s_timed_region": round(wall, 4),
         "launch_ms": per_launch,

@@ -26,7 +26,8 @@ fastest of those: 0.1-1.3 s per workload for the ones measured (14-84 candidates
 
 `HbmArena` owns one allocation that spans whole granules of the free
 device memory; callers take typed views of it at the offsets a `Placement`
-gives.  The kernels themselves are unchanged; this module only decides where
+gives, and allocate their other tensors (weights, other activations) from
+the arena's heap, the part of every granule outside the placement slots.  The kernels themselves are unchanged; this module only decides where
 their operands live.  It uses torch for the device allocation and for event
 timing.
 """
@@ -120,8 +121,67 @@ class Placement:
                 "ms_first_pass_worst": round(max(t[0] for t in first), 5)}
 
 
+class Heap:
+    """First-fit allocation of byte ranges inside a set of free extents (no
+    device memory of its own: HbmArena backs it).  Extents and blocks are
+    (offset, end) pairs; every block starts on an `align` boundary."""
+
+    def __init__(self, extents, align: int = ALIGN):
+        self.align = int(align)
+        self.free_list = sorted((int(a), int(b)) for a, b in extents if b > a)
+        self.used = {}
+
+    def alloc(self, nbytes: int) -> int:
+        """Offset of a new block of nbytes (ValueError if no extent fits)."""
+        n = round_up(max(1, int(nbytes)), self.align)
+        for i, (a, b) in enumerate(self.free_list):
+            start = round_up(a, self.align)
+            if start + n <= b:
+                rest = [(a, start)] if start > a else []
+                if start + n < b:
+                    rest.append((start + n, b))
+                self.free_list[i:i + 1] = rest
+                self.used[start] = start + n
+                return start
+        raise ValueError("no free extent holds %d bytes (largest free %d)"
+                         % (n, max((b - a for a, b in self.free_list), default=0)))
+
+    def free(self, offset: int) -> None:
+        """Return the block that starts at `offset`; neighbouring free extents merge."""
+        end = self.used.pop(int(offset))
+        merged = sorted(self.free_list + [(int(offset), end)])
+        out = []
+        for a, b in merged:
+            if out and a <= out[-1][1]:
+                out[-1] = (out[-1][0], max(out[-1][1], b))
+            else:
+                out.append((a, b))
+        self.free_list = out
+
+    @property
+    def free_bytes(self) -> int:
+        return sum(b - a for a, b in self.free_list)
+
+
+def heap_extents(granules: int):
+    """The parts of each granule outside its slot span (the span holds the
+    planned placements of streamed tensors)."""
+    out = []
+    for g in range(granules):
+        base = g * GRANULE
+        out.append((base, base + SLOT_START))
+        out.append((base + SLOT_START + SLOT_SPAN, base + GRANULE))
+    return out
+
+
 class HbmArena:
-    """One device allocation spanning whole granules of free HBM."""
+    """One device allocation spanning whole granules of free HBM.
+
+    The middle 16 GiB of each granule (its slot span) is where `plan` places
+    streamed tensors; the rest of every granule is a heap (`alloc`, `free`)
+    for the process's other tensors -- model weights, other activations --
+    so the arena can serve as the device memory of the whole process instead
+    of memory held back beside it."""
 
     def __init__(self, device=None, granules: int | None = None, keep_free: int = 24 << 30):
         import torch
@@ -136,6 +196,7 @@ class HbmArena:
                                                                       keep_free >> 30))
         self.granules = int(n)
         self.buf = torch.empty(self.granules * GRANULE, dtype=torch.uint8, device=self.device)
+        self.heap = Heap(heap_extents(self.granules))
 
     @property
     def nbytes(self) -> int:
@@ -149,6 +210,17 @@ class HbmArena:
             raise ValueError("view of %d bytes at offset %d is outside the arena (%d bytes) or "
                              "not 256-byte aligned" % (n, offset, self.nbytes))
         return self.buf[offset:offset + n].view(dtype).view(*shape)
+
+    def alloc(self, shape, dtype):
+        """A tensor from the arena's heap (outside the slot spans)."""
+        torch = self._torch
+        n = math.prod(shape) * torch.empty((), dtype=dtype).element_size()
+        return self.view(self.heap.alloc(n), shape, dtype)
+
+    def free(self, t) -> None:
+        """Return a tensor that alloc() gave to the heap (the caller drops its
+        references; the memory is reused by later alloc() calls)."""
+        self.heap.free(t.data_ptr() - self.buf.data_ptr())
 
     def release(self):
         """Drop the arena's reference; the memory returns to torch once no view

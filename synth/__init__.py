@@ -142,6 +142,16 @@ WORKLOADS = {w.name: w for w in [
              dists=_std_dists()),
     Workload("fused_ln_frame_b1_f49_l176400_d5120", 6, "fused", False, 1, 176400, 5120,
              (FRAME, 49), (FRAME, 49), dists=_std_dists()),
+    # the rest of the speed matrix (sglang PR #33144, "Speed Tests and
+    # Profiling": B1-L16, B2-L16 and B1-L90000 at D 5120 for both ops)
+    Workload("fused_ln_b2_l16_d5120", 7, "fused", False, 2, 16, 5120, (BCAST, 0), (BCAST, 0),
+             dists=_std_dists()),
+    Workload("nss_ln_b1_l16_d5120", 8, "nss", False, 1, 16, 5120, None, (BCAST, 0),
+             dists=_std_dists()),
+    Workload("nss_ln_b2_l16_d5120", 9, "nss", False, 2, 16, 5120, None, (BCAST, 0),
+             dists=_std_dists()),
+    Workload("nss_ln_b1_l90000_d5120", 10, "nss", False, 1, 90000, 5120, None, (BCAST, 0),
+             dists=_std_dists()),
 ]}
 
 

@@ -129,3 +129,36 @@ def test_place_streams_builds_typed_views(monkeypatch):
         t.zero_()
     y32.fill_(1.0)
     assert all(float(t.abs().sum()) == 0 for t in (*ins, y, outs[1]))
+
+
+def test_heap_first_fit_alignment_and_merge():
+    """The arena's heap: first fit, aligned blocks, freed neighbours merge."""
+    h = hbm.Heap([(0, 10 * hbm.ALIGN), (20 * hbm.ALIGN, 30 * hbm.ALIGN)])
+    a = h.alloc(3 * hbm.ALIGN)
+    b = h.alloc(1)                           # rounded up to one aligned block
+    assert (a, b) == (0, 3 * hbm.ALIGN)
+    c = h.alloc(8 * hbm.ALIGN)               # does not fit the rest of the first extent
+    assert c == 20 * hbm.ALIGN
+    assert h.free_bytes == 20 * hbm.ALIGN - 12 * hbm.ALIGN
+    with pytest.raises(ValueError):
+        h.alloc(7 * hbm.ALIGN)
+    h.free(a)
+    h.free(b)                                # merges with a's block and the tail
+    assert h.free_list[0] == (0, 10 * hbm.ALIGN)
+    assert h.alloc(10 * hbm.ALIGN) == 0
+    h.free(c)
+    assert (20 * hbm.ALIGN, 30 * hbm.ALIGN) in h.free_list
+
+
+def test_heap_extents_avoid_every_slot_span():
+    """Heap extents and placement slots never overlap, and together cover
+    every granule."""
+    ext = hbm.heap_extents(3)
+    assert sum(b - a for a, b in ext) == 3 * (hbm.GRANULE - hbm.SLOT_SPAN)
+    for g in range(3):
+        lo, hi = g * hbm.GRANULE + hbm.SLOT_START, g * hbm.GRANULE + hbm.SLOT_START + hbm.SLOT_SPAN
+        assert all(b <= lo or a >= hi for a, b in ext)
+    # every offset a placement can use lies in a slot span
+    r, w = hbm.offsets(0, (1, 2), [1 << 30, 1 << 30], [1 << 30, [1 << 30, 1 << 29]])
+    for off in r + [w[0], *w[1]]:
+        assert all(not (a <= off < b) for a, b in ext)

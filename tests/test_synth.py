@@ -60,3 +60,9 @@ def test_workload_table_matches_pages_shapes():
     assert w["fused_rms_w_b1_l90000_d10240"].algorithmic_bytes() == 11059240960
     assert w["fused_ln_b1_l16_d5120"].algorithmic_bytes() == 686080
     assert w["fused_rms_w_b2_l16_d10240"].algorithmic_bytes() == 3973120
+    # the rest of the pages' speed matrix at D 5120
+    assert w["fused_ln_b2_l16_d5120"].algorithmic_bytes() == 32 * 4 * 10240 + 3 * 10240
+    assert w["nss_ln_b1_l16_d5120"].algorithmic_bytes() == 16 * 2 * 10240 + 2 * 10240
+    assert w["nss_ln_b2_l16_d5120"].algorithmic_bytes() == 32 * 2 * 10240 + 2 * 10240
+    assert w["nss_ln_b1_l90000_d5120"].algorithmic_bytes() == 90000 * 2 * 10240 + 2 * 10240
+    assert len({x.wid for x in w.values()}) == len(w)     # one generator key space each
