@@ -123,14 +123,15 @@ int hbm_streams(uint32_t flags, bool fused, rn_layout gate_layout, rn_layout ss_
   return n;
 }
 
-// Rows a multiple of 8 KB apart (D % 4096 == 0): shapes whose waves each
-// stream a long exact-cover span of such rows run in one of two modes from
-// one process to the next on MI355X (the fused op at D = 4096 with one wave
-// x 8 vectors: 1.20-1.28 ms in some processes, 1.38-1.42 ms in others, the
-// same code and addresses), which rotating each row's vector order did not
-// remove.  Two waves x 4 vectors measured faster in both modes (1.24 / 1.31
-// ms without affine, 1.25 / 1.27 ms with binary32 weight/bias), so the
-// fused op there takes at least this many waves per row.
+// Rows a multiple of 8 KB apart (D % 4096 == 0): the fused op there takes at
+// least this many waves per row.  Measured in one process at D = 4096,
+// 220500 rows: two waves x 4 vectors 69.5 % of 8 TB/s against 65.2 % for
+// one wave x 8 on torch's back-to-back allocations (every stream in one
+// third of physical HBM), but 80.8 % against 83.5 % with the outputs in two
+// other thirds.  The rule keeps the gain for ordinary allocations, the
+// common case, at a 3 % cost on a planned placement.  (Earlier sweeps had
+// seen the one-wave shape switch between two speeds from one process to
+// the next; the placement of the tensors in HBM explains that.)
 constexpr int kFusedPow2MinWaves = 2;
 
 // Whether every aligned group of k consecutive rows (rows k*m .. k*m + k - 1)
@@ -199,7 +200,10 @@ int shape_for(int64_t R, int64_t L, int64_t D, uint32_t flags, bool fused, int a
   // Large problems: the norm-only op without affine streams its rows best
   // with 8 vectors per lane where the first fit would be 6 (2 or 4 waves per
   // row; a sweep of every shape at ~903 M elements, D = 5632-6144 and
-  // 10752-12288: 2.3-6.5 % faster, e.g. D = 12288 0.638 -> 0.599 ms).
+  // 10752-12288: 2.3-6.5 % faster, e.g. D = 12288 0.638 -> 0.599 ms;
+  // re-measured in one process, D 6144 / 12288: 75.5 / 75.7 % vs 71.5 /
+  // 71.3 % of 8 TB/s on back-to-back allocations, 78.3 / 77.8 % vs 75.8 /
+  // 75.3 % with the outputs in another third).
   const bool nss_plain = !fused && !(flags & RN_WEIGHT);
   // Large norm-only problems run one-wave shapes of 8 or 10 vectors per lane
   // with 2 rows per workgroup (the twins after the multi-row shapes).

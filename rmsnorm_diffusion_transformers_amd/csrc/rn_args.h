@@ -14,7 +14,12 @@ constexpr int kWaveSize = 64;
 // covers rows of up to 64 * W * VPT vectors (D = 512 * W * VPT); tail lanes of
 // shorter rows are masked.
 //
-// Choice (measured on MI355X; each rule from sweeps over every compiled shape):
+// Choice (measured on MI355X; each rule from sweeps over every compiled shape).
+// The large-problem rules were re-measured in one process on two placements
+// of the tensors -- torch's back-to-back allocations (every stream in one
+// third of physical HBM) and a spread placement (the outputs in two other
+// thirds) -- each pick against the shape it displaces; the figures are
+// rule pick vs displaced shape, in % of 8 TB/s:
 //   * a problem that streams at most 4 tensors through HBM (x, y, and the
 //     residual pair of the fused op; broadcast / per-frame modulation rows
 //     come from L2) and has more than kMidRows rows runs best with long
@@ -23,7 +28,10 @@ constexpr int kWaveSize = 64;
 //     wave per row at D = 5120 (L = 90000-176400);
 //   * a problem that also streams per-row scale/shift (or a per-row gate)
 //     runs best with 10 waves per row and 1-4 vectors per lane (shorter
-//     per-wave spans and more rows in flight), once D >= kManyStreamsMinD;
+//     per-wave spans and more rows in flight), once D >= kManyStreamsMinD
+//     (fused RMS + weight, D 10240: 75.9 vs 73.3 back to back, 81.9 vs
+//     82.3 spread; fused LN, D 5120: 74.6 vs 71.7, 81.1 vs 81.5 -- a gain
+//     where the streams share a third, a wash where they do not);
 //   * from D >= kSplitMinD, problems of a few hundred rows leave most SIMDs
 //     idle with one wave per row and are bound by each row's load -> reduce
 //     -> store chain, so the row is split so that each wave holds 2-5
@@ -50,7 +58,9 @@ constexpr int kWaveSize = 64;
 //     elements up, D = 512 to 10240, by 0.5-66 % (D = 5120, L = 176400:
 //     binary32 weight/bias 0.69 -> 0.61 ms, bf16 0.92 -> 0.61 ms), and
 //     slower below about 8 M elements, where 4x fewer waves leave part of
-//     the chip idle.  K = 4 beat K = 2 and
+//     the chip idle (re-measured, binary32 / bf16 weight+bias at D 5120 and
+//     binary32 at D 2048: 73.8 / 74.2 / 79.0 vs 66.0 / 70.8 / 62.6 back to
+//     back, 77.3 / 77.4 / 79.5 vs 66.5 / 72.8 / 64.2 spread).  K = 4 beat K = 2 and
 //     K = 8; prefetching the next row before the current row's stores did
 //     not help on balance.  The fused op and the norm-only op without
 //     affine ran slower as multi-row shapes.
@@ -59,9 +69,10 @@ constexpr int kWaveSize = 64;
 //     workgroup instead of 4 (the twins at the end of the table): with the
 //     tensors at a measured HBM placement, D = 5120 78.0 -> 79.5 % of 8 TB/s
 //     and D = 4096 78.8-79.6 -> 80.0 %; on back-to-back allocations within
-//     +-0.4 % at D = 5120 and 74.4 -> 75.6 % at D = 4096.  At 4 vectors per
-//     lane 2 rows per workgroup were slower (D = 2048: 81.1 -> 80.2 %), at 6
-//     the same.
+//     +-0.4 % at D = 5120 and 74.4 -> 75.6 % at D = 4096 (re-measured: D 5120
+//     75.0 vs 75.3 back to back, 79.1 vs 77.6 spread; D 4096 76.5 vs 75.1,
+//     80.3 vs 78.9).  At 4 vectors per lane 2 rows per workgroup were slower
+//     (D = 2048: 81.1 -> 80.2 %), at 6 the same.
 struct Shape {
   int w;
   int vpt;
@@ -103,7 +114,9 @@ constexpr int kVgprBudget = 52;
 // the fused op with gate.  Its tighter budget moves it to 2 x 5 vectors at
 // D = 4608-5120 and 4 x 5 at D = 8704-10240, measured 21 % and 24-32 %
 // faster at 16384-176400 rows with per-row scale/shift (which keeps it off
-// the multi-row shapes) and no slower on small problems.
+// the multi-row shapes) and no slower on small problems (re-measured, bf16
+// weight + bias, per-row scale/shift, D 5120: 77.4 vs 62.8 back to back,
+// 79.7 vs 63.2 spread).
 constexpr int kVgprBudgetNormAffine = 48;
 // Spacing of loads / stores, in units of 8 cycles (s_nop 7); the streamed
 // row loads of the fused op with one wave per row, and of the norm-only op

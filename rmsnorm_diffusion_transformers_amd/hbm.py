@@ -2,27 +2,27 @@
 
 The row kernels stream every input once and write every output once, so
 their rate is set by HBM.  On MI355X that rate also depends on where the
-tensors sit in device memory, not only on how the kernel accesses them.
+tensors sit in physical memory, not only on how the kernel accesses them.
 Measured with the fused LayerNorm kernel at B 1, L 176400, D 5120 (four
-1.8 GB streams: x and residual read, y and residual_out written) placed at
-controlled offsets of one large allocation:
+1.8 GB streams: x and residual read, y and residual_out written):
 
-  * the device address space splits into 32 GiB granules.  Within a granule
-    the rate does not depend on the offset of a tensor (0.25 to 32 MB shifts:
-    no effect), but each granule falls into one of a few classes;
-  * both output streams in granules of one class: 74-77 % of 8 TB/s.  That is
-    the case for tensors allocated back to back (they share a granule), which
-    is what a caching allocator gives on a fresh device;
-  * the inputs in one class and each output in its own other class: 82-83 %.
-    Other assignments fall in between (79-82 %);
-  * the pattern holds for the other workloads measured (the fused op at
-    L 90000 D 5120 and at D 10240 with per-row scale/shift, the norm-only op).
+  * what matters is which third of the device's physical memory (three
+    regions of 96 GiB on the 288 GiB part) each stream lies in.  Inside one
+    large allocation, with the inputs fixed, one output fixed and the other
+    moved in 512 MiB steps, the rate is flat inside a region and steps at
+    its edges (96 GiB apart); shifts of 4 KiB to 256 MiB change nothing;
+  * both outputs in one third: 76 % (first third) or 79.5 % of 8 TB/s;
+    the outputs in two different thirds: 82-83 %.  torch's back-to-back
+    allocations put all four streams in one third: 75 %;
+  * a larger allocation's pages come in varying physical order, so a
+    fixed offset rule does not guarantee distinct thirds, and user space
+    sees no physical address.
 
-The driver does not expose the classes, so `plan` measures them.  It packs
-the inputs into one granule, tries every assignment of the outputs to other
-granules (with two choices of the input granule), times the actual launch
-for each, times the three fastest again with more launches, and keeps the
-fastest of those: 0.1-1.3 s per workload for the ones measured (14-84 candidates).
+So `plan` measures.  It packs the inputs into one 32 GiB granule of an
+arena, tries every assignment of the outputs to other granules (with two
+choices of the input granule), times the actual launch for each, times the
+three fastest again with more launches, and keeps the fastest of those:
+about 0.8 s for the headline workload (84 candidates).
 
 `HbmArena` owns one allocation that spans whole granules of the free
 device memory; callers take typed views of it at the offsets a `Placement`
@@ -37,7 +37,7 @@ import itertools
 import math
 from dataclasses import dataclass, field
 
-GRANULE = 32 << 30          # bytes of device address space that share one class
+GRANULE = 32 << 30          # unit of the placement search (a third of HBM is 3 of them)
 SLOT_START = 8 << 30        # first byte used inside a granule (clear of its edges)
 SLOT_SPAN = 16 << 30        # bytes usable per granule from SLOT_START
 ALIGN = 2 << 20             # tensors start on 2 MiB boundaries
