@@ -237,9 +237,10 @@ def plan(arena: HbmArena, read_bytes, write_bytes, make_launch, read_granules: i
     that enqueues the operation on views of `arena` at those offsets.  Every
     candidate is timed over `steps` launches; the `refine` fastest are timed
     again over `refine_steps` launches and the choice is made on those, so that
-    a short trial's noise does not decide it.  Each input region is
-    zero-filled before it is first timed, so that no trial reads uninitialised
-    memory."""
+    a short trial's noise does not decide it.  Each input region is filled
+    with standard normal bf16 values before it is first timed, so that no
+    trial reads uninitialised memory and the trials stream data like the
+    real inputs rather than zeros."""
     torch = arena._torch
     st = stream if stream is not None else torch.cuda.current_stream(arena.device)
 
@@ -262,7 +263,11 @@ def plan(arena: HbmArena, read_bytes, write_bytes, make_launch, read_granules: i
         if rg not in filled:
             r_off, _ = offsets(rg, wg, read_bytes, write_bytes)
             for off, nb in zip(r_off, read_bytes):
-                arena.buf[off:off + nb].zero_()
+                region = arena.buf[off:off + nb]
+                if nb % 2 == 0:
+                    region.view(torch.bfloat16).normal_()
+                else:
+                    region.zero_()
             filled.add(rg)
         trials.append((timed(rg, wg, steps), rg, wg))
     finals = [(timed(rg, wg, refine_steps), rg, wg) for _, rg, wg in sorted(trials, key=lambda t: t[0])[:refine]]
