@@ -35,9 +35,9 @@ plain elementwise copy, used to scale rocprof byte counters), --no-cpu-baseline,
 --no-extras, --no-companion, --workload NAME, --placement-map (the granule class
 map of the headline kernel), --placement-thirds (its rate against the outputs'
 place in one large allocation at 512 MiB steps), --placement-counters (three
-placements, 40 launches each, for rocprofv3 counter runs), --placement-widths
-(torch's allocations against a planned placement at row widths 2048-10240);
-each of the placement modes prints one JSON line of its own.
+placements, 40 warm + 40 measured launches each, for rocprofv3 counter runs),
+--placement-widths (torch's allocations against a planned placement at row
+widths 2048-10240); each of the placement modes prints one JSON line of its own.
 """
 from __future__ import annotations
 
@@ -655,14 +655,15 @@ def placement_thirds(rn, dev, step_gib=0.5):
 
 
 def placement_counters(rn, dev, n=40):
-    """The headline kernel on three placements, n launches each, in this order:
-    torch's back-to-back allocations; one large allocation with both outputs in
-    its first third (residual_out at 40 GiB, y at 60 GiB); the same with the
-    outputs in two thirds (y at 150 GiB).  A counter trace of this command
-    splits by dispatch index (0..n-1, n..2n-1, 2n..3n-1) of the row kernel;
-    each group follows 0.2 s of plain copies (another kernel) that lift the
-    GPU out of its idle clocks.  Without a profiler the printed line gives
-    each placement's rate from its n launches."""
+    """The headline kernel on three placements, 2n launches each, in this
+    order: torch's back-to-back allocations; one large allocation with both
+    outputs in its first third (residual_out at 40 GiB, y at 60 GiB); the
+    same with the outputs in two thirds (y at 150 GiB).  Each placement's
+    first n launches bring the GPU out of its idle clocks and its last n are
+    the measured ones, so a counter trace of this command splits by
+    row-kernel dispatch index (measured: n..2n-1, 3n..4n-1, 5n..6n-1).
+    Without a profiler the printed line gives each placement's rate from its
+    measured launches."""
     import torch
 
     from rmsnorm_diffusion_transformers_amd import hbm
@@ -671,11 +672,12 @@ def placement_counters(rn, dev, n=40):
     R, D = wl.R, wl.D
     res = {}
 
-    def run(name, call, y):
-        # warm the GPU out of its idle clocks first, with a plain copy into
-        # the output (another kernel, so the row-kernel dispatches stay n per
-        # placement)
-        settle(lambda: torch.neg(y, out=y), 0.2)
+    def run(name, call):
+        # n launches to bring the GPU out of its idle clocks, then n timed
+        # (a fixed count, so a counter trace splits by dispatch index)
+        for _ in range(n):
+            call()
+        torch.cuda.synchronize()
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record()
         for _ in range(n):
@@ -688,7 +690,7 @@ def placement_counters(rn, dev, n=40):
 
     x, r = upload({"x": inp["x"]}, dev)["x"], upload({"r": inp["residual"]}, dev)["r"]
     y, o = torch.empty_like(x), torch.empty_like(x)
-    run("torch_allocations", make(x, r, y, o), y)
+    run("torch_allocations", make(x, r, y, o))
     del x, r, y, o
     torch.cuda.empty_cache()
     arena = hbm.HbmArena(dev)
@@ -696,8 +698,8 @@ def placement_counters(rn, dev, n=40):
     x, r = view(0), view(2 * GiB)
     x.copy_(host_bf16(inp["x"]))
     r.copy_(host_bf16(inp["residual"]))
-    run("outputs_in_one_third", make(x, r, view(60 * GiB), view(40 * GiB)), view(60 * GiB))
-    run("outputs_in_two_thirds", make(x, r, view(150 * GiB), view(40 * GiB)), view(150 * GiB))
+    run("outputs_in_one_third", make(x, r, view(60 * GiB), view(40 * GiB)))
+    run("outputs_in_two_thirds", make(x, r, view(150 * GiB), view(40 * GiB)))
     del x, r
     arena.release()
     print(json.dumps({"workload": wl.name, "launches_each": n, "frac": res}), flush=True)
@@ -843,8 +845,8 @@ def main():
                     help="the headline kernel's rate against where its outputs sit in one large "
                          "allocation, at 512 MiB steps")
     ap.add_argument("--placement-counters", action="store_true",
-                    help="the headline kernel on three placements, 40 launches each, for a "
-                         "rocprofv3 counter run")
+                    help="the headline kernel on three placements, 40 warm + 40 measured "
+                         "launches each, for rocprofv3 counter runs")
     ap.add_argument("--placement-widths", action="store_true",
                     help="torch's allocations against a planned placement for the fused and "
                          "norm-only ops at several row widths")

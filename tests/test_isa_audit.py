@@ -195,3 +195,27 @@ def test_multi_row_rms_partials_alternate_copies(nss_rms_asm, shape, w, rpb, vpt
     assert offs[0] == offs[2] and offs[1] == offs[3], offs
     nred = w * rpb
     assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == 2 * 2 * nred * 4
+
+
+@pytest.mark.parametrize("shape,w,rpb,vpt", [(29, 2, 2, 3), (31, 2, 2, 5), (32, 4, 1, 3), (34, 4, 1, 5)])
+@pytest.mark.parametrize("aff", [2, 4])
+def test_multi_row_layernorm_partials_alternate_copies(nss_asm, shape, w, rpb, vpt, aff):
+    """The LayerNorm multi-row kernels with several waves per row: the first
+    LDS write of each of the 4 rows (its partial sum) alternates between two
+    copies, and the workgroup holds two copies of each of the three partial
+    arrays (sum, sum of squares, and the maximum of the overflow path)."""
+    sym = "_ZN2rn10row_kernelINS_2OpILb0ELb0ELb0ELi%dELi0EEELi%dEEEvNS_7RowArgsE" % (aff, shape)
+    body, meta = _kernel(nss_asm, sym)
+    lines = body.splitlines()
+    stores = [i for i, ln in enumerate(lines) if re.match(r"\s+buffer_store_dwordx4\b", ln)]
+    assert len(stores) == 4 * vpt
+    ends = [stores[vpt * k + vpt - 1] for k in range(4)]
+    starts = [0] + [e + 1 for e in ends[:-1]]
+    offs = []
+    for a, b in zip(starts, ends):
+        first = next(ln for ln in lines[a:b] if re.match(r"\s+ds_write_b32\b", ln))
+        m = re.search(r"offset:(\d+)", first)
+        offs.append(int(m.group(1)) if m else 0)
+    assert all(offs[k] != offs[k + 1] for k in range(3)), offs
+    assert offs[0] == offs[2] and offs[1] == offs[3], offs
+    assert _meta_int(meta, "amdhsa_group_segment_fixed_size") == 2 * 3 * w * rpb * 4

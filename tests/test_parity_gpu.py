@@ -293,6 +293,71 @@ def test_empty_and_side_stream(rn, orc):
     compare_outputs(to_host(y), y_ref, what="side stream")
 
 
+def test_repeated_calls_and_prepared_calls(rn, orc):
+    """The library keeps each thread's last validated call with its launch
+    plan, and rn.prepare checks a call once: alternating two problems (A, B,
+    A, B) must launch each with its own arguments every time, a repeated
+    identical call must pick up new input contents, and a prepared call must
+    give the direct call's bits."""
+    import torch
+    D = 5120
+    probs = []
+    for seed, L in ((61, 96), (62, 40)):
+        inp = _small_problem(seed, True, False, (BCAST, 0), 0, (BCAST, 0), 1, L, D)
+        d = {k: to_dev(v) for k, v in inp.items()}
+        y, ro = torch.empty_like(d["x"]), torch.empty_like(d["x"])
+        ref = orc.fused(inp["x"], inp["residual"], inp["gate"], None, None, inp["scale"],
+                        inp["shift"], 1, L, D, False, (BCAST, 0), (BCAST, 0), 1e-6)
+        probs.append((inp, d, y, ro, L, ref))
+
+    def call(p):
+        inp, d, y, ro, L, ref = p
+        rn.resnorm_fused_fwd(y, ro, d["x"], d["residual"], d["gate"], None, None, d["scale"],
+                             d["shift"], 1, L, D, rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6)
+
+    for k in range(4):
+        p = probs[k % 2]
+        p[2].fill_(float("nan"))
+        p[3].fill_(float("nan"))
+        call(p)
+        torch.cuda.synchronize()
+        compare_outputs(to_host(p[2]), p[5][0], to_host(p[3]), p[5][1], "alternating call %d" % k)
+    # the same call again after new inputs were written into the same buffers
+    inp, d, y, ro, L, _ = probs[0]
+    x2 = synth.random_bf16((L, D), 63, 1)
+    d["x"].copy_(to_dev(x2))
+    call(probs[0])
+    call(probs[0])
+    torch.cuda.synchronize()
+    ref2 = orc.fused(x2, inp["residual"], inp["gate"], None, None, inp["scale"], inp["shift"], 1, L,
+                     D, False, (BCAST, 0), (BCAST, 0), 1e-6)
+    compare_outputs(to_host(y), ref2[0], to_host(ro), ref2[1], "repeat after new inputs")
+    # a prepared call gives the direct call's bits, also after new inputs
+    y_direct = y.clone()
+    y.fill_(float("nan"))
+    launch = rn.prepare(rn.resnorm_fused_fwd, y, ro, d["x"], d["residual"], d["gate"], None, None,
+                        d["scale"], d["shift"], 1, L, D, rn.RN_GATE, (BCAST, 0), (BCAST, 0), 1e-6)
+    launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_direct.view(torch.int16))
+    d["x"].copy_(to_dev(inp["x"]))
+    launch()
+    torch.cuda.synchronize()
+    compare_outputs(to_host(y), probs[0][5][0], to_host(ro), probs[0][5][1], "prepared call")
+    # the _ex form through prepare: binary32 output against the oracle's binary32
+    # y, at the binary32-output tests' bound (2^-14 relative, absolute below 1)
+    y32 = torch.empty((L, D), dtype=torch.float32, device="cuda")
+    launch32 = rn.prepare(rn.norm_scale_shift_fwd_ex, y32, d["x"], None, None, d["scale"], d["shift"],
+                          1, L, D, 0, (BCAST, 0), 1e-6, y_dtype=rn.RN_DTYPE_F32)
+    launch32()
+    torch.cuda.synchronize()
+    ref32 = orc.nss(inp["x"], None, None, inp["scale"], inp["shift"], 1, L, D, False, (BCAST, 0),
+                    1e-6, y_dtype=oracle.Y_F32)[0]
+    got = y32.cpu().numpy().astype(np.float64).ravel()
+    want = np.asarray(ref32, dtype=np.float64).ravel()
+    assert np.all(np.abs(got - want) <= 2.0 ** -14 * np.maximum(1.0, np.abs(want)))
+
+
 def test_gpu_norm_invariants(rn, orc):
     """Pure-norm GPU outputs (scale = shift = 0, no affine) at D >= 512.
 
