@@ -1,7 +1,10 @@
-"""Build the gfx950 HIP library (librnorm.so) in-tree with hipcc.
+"""Build the gfx950 HIP libraries in-tree with hipcc.
 
-Every translation unit under csrc/ is compiled for gfx950 only, in parallel,
-then linked into one shared library next to this file.
+librnorm.so: every translation unit under csrc/, compiled for gfx950 only, in
+parallel, then linked into one shared library next to this file.
+libtrafficref.so: the measurement reference under csrc/ref/ (a kernel with
+the fused op's memory traffic and none of its arithmetic, which the
+benchmark times beside the fused kernel); not part of the operation.
 """
 from __future__ import annotations
 
@@ -14,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librnorm.so")
+REF_LIB = os.path.join(HERE, "libtrafficref.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
@@ -25,6 +29,10 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def ref_sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "ref", "*.hip")))
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC, *HIP_FLAGS, "-I", CSRC, "-c", src, "-o", obj]
@@ -34,19 +42,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile and link librnorm.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or max(1, min(len(srcs), os.cpu_count() or 1))
-    with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile and link librnorm.so and libtrafficref.so; returns librnorm.so's
+    path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs, refs = sources(), ref_sources()
+    jobs = jobs or max(1, min(len(srcs) + len(refs), os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs + refs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], REF_LIB)
     return LIB
 
 

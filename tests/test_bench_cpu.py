@@ -69,3 +69,23 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert out.returncode == 2
     assert "exactly one GPU" in out.stderr and "--gpus 2" in out.stderr
     assert out.stdout == ""
+
+
+def test_traffic_reference_library_refuses_what_it_does_not_take():
+    """The measurement reference (libtrafficref.so) loads without a GPU and
+    refuses, before any launch, the arguments it does not take; an empty
+    problem is a no-op."""
+    import ctypes
+    lib = ctypes.CDLL(bench.REF_LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    f = lib.rn_traffic_ref
+    f.argtypes = [P] * 7 + [I64] * 4 + [P]
+    f.restype = ctypes.c_int
+    p = [4096 * (i + 1) for i in range(7)]
+    assert f(*p, 1, 16, 4096, 1, None) == 1          # D other than 5120
+    assert f(*p, 1, 16, 5120, 3, None) == 1          # L not a multiple of frames
+    assert f(*p, 1, 16, 5120, 0, None) == 1          # no frames
+    assert f(*p, -1, 16, 5120, 1, None) == 1
+    assert f(*p, 1, 1 << 31, 5120, 1, None) == 1     # more than 2^31 - 1 rows
+    assert f(*([None] * 7), 1, 16, 5120, 1, None) == 1
+    assert f(*([None] * 7), 0, 16, 5120, 1, None) == 0   # empty: nothing launched
