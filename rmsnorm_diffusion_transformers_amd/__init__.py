@@ -130,27 +130,6 @@ def _torch_mod():
     return _torch
 
 
-def _addr(t, dtype=RN_DTYPE_BF16):
-    """Device address of a contiguous CUDA tensor of the given element type
-    (or an int address, or None).  Runs on every call, so it sticks to cheap
-    attribute checks."""
-    if t is None:
-        return None
-    if isinstance(t, int):
-        return t
-    torch = _torch_mod()
-    if not isinstance(t, torch.Tensor):
-        raise TypeError("expected a torch.Tensor, an int address or None, got %r" % type(t))
-    if not t.is_cuda:
-        raise ValueError("tensor must be on a GPU device (got %s); there is no CPU path" % t.device)
-    want = _TORCH_DTYPES[dtype]
-    if t.dtype != want:
-        raise TypeError("tensor must be %s (got %s)" % (want, t.dtype))
-    if not t.is_contiguous():
-        raise ValueError("tensor must be contiguous")
-    return t.data_ptr()
-
-
 def _dtype_code(dt) -> int:
     import torch
     if dt is None or dt == torch.bfloat16:
@@ -164,20 +143,36 @@ def _dtype_code(dt) -> int:
 
 def _rows(lay, B: int, L: int) -> int:
     kind, frames = (lay.kind, lay.frames) if isinstance(lay, rn_layout) else lay
-    return {RN_BCAST: 1, RN_ROW: B * L, RN_FRAME: B * frames}.get(int(kind), 0)
+    kind = int(kind)
+    if kind == RN_BCAST:
+        return 1
+    if kind == RN_ROW:
+        return B * L
+    if kind == RN_FRAME:
+        return B * int(frames)
+    return 0
 
 
-def _check_tensors(named):
-    """Host-side checks of the tensors an entry point receives (int addresses
-    are passed through unchecked): one common device, and at least as many
-    elements as the sizes and layouts make the kernel touch.  `named` is a
-    sequence of (name, tensor or address or None, elements needed).  Returns
-    the device index (None when only addresses were given)."""
+def _operands(named):
+    """One pass over the operands of an entry point.  `named` is a sequence of
+    (name, tensor or int address or None, elements needed, RN_DTYPE_* code).
+    A tensor must hold at least as many elements as the sizes and layouts make
+    the kernel touch, share one device with the other tensors, have the
+    element type of its code (not checked for a code the library does not
+    define: the library rejects that) and be contiguous.  Int addresses are
+    passed through unchecked.  Returns (GPU index or None, addresses).  Host
+    tensors pass the size and device checks and are then refused: there is
+    no CPU path."""
     Tensor = _torch_mod().Tensor
     dev = first = None
-    for name, t, need in named:
-        if not isinstance(t, Tensor):
+    ptrs = []
+    for name, t, need, code in named:
+        if t is None or isinstance(t, int):
+            ptrs.append(t)
             continue
+        if not isinstance(t, Tensor):
+            raise TypeError("%s: expected a torch.Tensor, an int address or None, got %r"
+                            % (name, type(t)))
         if t.numel() < need:
             raise ValueError("%s has %d elements; the sizes and layout need %d" % (name, t.numel(), need))
         d = t.get_device()   # GPU index; -1 for host and meta tensors
@@ -185,88 +180,118 @@ def _check_tensors(named):
             dev, first = d, t
         elif d != dev or (d < 0 and t.device != first.device):
             raise ValueError("%s is on %s but other operands are on %s" % (name, t.device, first.device))
-    return dev if dev is not None and dev >= 0 else None
+        want = _TORCH_DTYPES.get(code)
+        if want is not None and t.dtype != want:
+            raise TypeError("%s must be %s (got %s)" % (name, want, t.dtype))
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+        ptrs.append(t.data_ptr() if d >= 0 else None)
+    if first is not None and dev < 0:
+        raise ValueError("tensors must be on a GPU device (got %s); there is no CPU path"
+                         % first.device)
+    return (dev if first is not None else None), ptrs
+
+
+def _check_tensors(named):
+    """_operands over (name, tensor or address or None, elements needed) with
+    no element type check; returns the GPU index (None when only addresses
+    were given)."""
+    return _operands([(n, t, need, None) for n, t, need in named])[0]
 
 
 def _stream(stream, device=None):
-    """The stream to enqueue on: the given one, else torch's current stream of
-    the operands' device."""
+    """The stream to enqueue on: the given one (a torch stream or a raw
+    handle), else torch's current stream of the operands' device."""
     if stream is None:
-        return _torch_mod().cuda.current_stream(device).cuda_stream
+        torch = _torch_mod()
+        return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
 
 
+_LAYOUTS = {}   # (kind, frames) -> rn_layout (passed by value; never modified)
+
+
 def _layout(lay) -> rn_layout:
     if isinstance(lay, rn_layout):
         return lay
-    kind, frames = lay
-    return rn_layout(int(kind), int(frames))
+    c = _LAYOUTS.get(lay) if isinstance(lay, tuple) else None
+    if c is None:
+        kind, frames = lay
+        c = rn_layout(int(kind), int(frames))
+        if isinstance(lay, tuple) and len(_LAYOUTS) < 4096:
+            _LAYOUTS[lay] = c
+    return c
+
+
+def _fused_operands(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
+                    gate_layout, ss_layout, affine_dtype, y_dtype, y_scale):
+    n, ss = B * L * D, _rows(ss_layout, B, L) * D
+    return _operands((("y", y, n, y_dtype), ("residual_out", residual_out, n, RN_DTYPE_BF16),
+                      ("x", x, n, RN_DTYPE_BF16), ("residual", residual, n, RN_DTYPE_BF16),
+                      ("gate", gate, _rows(gate_layout, B, L) * D, RN_DTYPE_BF16),
+                      ("weight", weight, D, affine_dtype), ("bias", bias, D, affine_dtype),
+                      ("scale", scale, ss, RN_DTYPE_BF16), ("shift", shift, ss, RN_DTYPE_BF16),
+                      ("y_scale", y_scale, B * L, RN_DTYPE_F32)))
+
+
+def _nss_operands(y, x, weight, bias, scale, shift, B, L, D, ss_layout, affine_dtype, y_dtype,
+                  y_scale):
+    n, ss = B * L * D, _rows(ss_layout, B, L) * D
+    return _operands((("y", y, n, y_dtype), ("x", x, n, RN_DTYPE_BF16),
+                      ("weight", weight, D, affine_dtype), ("bias", bias, D, affine_dtype),
+                      ("scale", scale, ss, RN_DTYPE_BF16), ("shift", shift, ss, RN_DTYPE_BF16),
+                      ("y_scale", y_scale, B * L, RN_DTYPE_F32)))
 
 
 def _args_fused(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D, flags,
                 gate_layout, ss_layout, eps, stream, affine_dtype, y_dtype, y_scale):
     """Checked C arguments of resnorm_fused_fwd_ex."""
-    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
-                        gate_layout, ss_layout, y_scale)
-    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    B, L, D, affine_dtype, y_dtype = int(B), int(L), int(D), int(affine_dtype), int(y_dtype)
+    dev, p = _fused_operands(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L,
+                             D, gate_layout, ss_layout, affine_dtype, y_dtype, y_scale)
+    ext = rn_ext(affine_dtype, y_dtype, p[9])
     return (_lib.resnorm_fused_fwd_ex,
-            (_addr(y, y_dtype), _addr(residual_out), _addr(x), _addr(residual), _addr(gate),
-             _addr(weight, affine_dtype), _addr(bias, affine_dtype), _addr(scale), _addr(shift),
-             int(B), int(L), int(D), int(flags), _layout(gate_layout), _layout(ss_layout),
-             float(eps), ctypes.byref(ext), _stream(stream, dev)), ext)
+            (*p[:9], B, L, D, int(flags), _layout(gate_layout), _layout(ss_layout), float(eps),
+             ctypes.byref(ext), _stream(stream, dev)), ext)
 
 
 def _args_nss(y, x, weight, bias, scale, shift, B, L, D, flags, ss_layout, eps, stream,
               affine_dtype, y_dtype, y_scale):
     """Checked C arguments of norm_scale_shift_fwd_ex."""
-    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale)
-    ext = rn_ext(int(affine_dtype), int(y_dtype), _addr(y_scale, RN_DTYPE_F32))
+    B, L, D, affine_dtype, y_dtype = int(B), int(L), int(D), int(affine_dtype), int(y_dtype)
+    dev, p = _nss_operands(y, x, weight, bias, scale, shift, B, L, D, ss_layout, affine_dtype,
+                           y_dtype, y_scale)
+    ext = rn_ext(affine_dtype, y_dtype, p[6])
     return (_lib.norm_scale_shift_fwd_ex,
-            (_addr(y, y_dtype), _addr(x), _addr(weight, affine_dtype), _addr(bias, affine_dtype),
-             _addr(scale), _addr(shift), int(B), int(L), int(D), int(flags), _layout(ss_layout),
-             float(eps), ctypes.byref(ext), _stream(stream, dev)), ext)
+            (*p[:6], B, L, D, int(flags), _layout(ss_layout), float(eps), ctypes.byref(ext),
+             _stream(stream, dev)), ext)
 
 
 def resnorm_fused_fwd(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
                       flags, gate_layout=(RN_BCAST, 0), ss_layout=(RN_BCAST, 0), eps=1e-6,
                       stream=None) -> None:
     """Enqueue the fused op (C entry point of the same name); raises RnError."""
-    dev = _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
-                        gate_layout, ss_layout, None)
-    _check(_lib.resnorm_fused_fwd(_addr(y), _addr(residual_out), _addr(x), _addr(residual),
-                                  _addr(gate), _addr(weight), _addr(bias), _addr(scale),
-                                  _addr(shift), int(B), int(L), int(D), int(flags),
-                                  _layout(gate_layout), _layout(ss_layout), float(eps),
-                                  _stream(stream, dev)))
-
-
-def _fused_checks(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L, D,
-                  gate_layout, ss_layout, y_scale):
     B, L, D = int(B), int(L), int(D)
-    n, ss = B * L * D, _rows(ss_layout, B, L) * D
-    return _check_tensors((("y", y, n), ("residual_out", residual_out, n), ("x", x, n),
-                           ("residual", residual, n), ("gate", gate, _rows(gate_layout, B, L) * D),
-                           ("weight", weight, D), ("bias", bias, D), ("scale", scale, ss),
-                           ("shift", shift, ss), ("y_scale", y_scale, B * L)))
-
-
-def _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, y_scale):
-    B, L, D = int(B), int(L), int(D)
-    n, ss = B * L * D, _rows(ss_layout, B, L) * D
-    return _check_tensors((("y", y, n), ("x", x, n), ("weight", weight, D), ("bias", bias, D),
-                           ("scale", scale, ss), ("shift", shift, ss), ("y_scale", y_scale, B * L)))
+    dev, p = _fused_operands(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L,
+                             D, gate_layout, ss_layout, RN_DTYPE_BF16, RN_DTYPE_BF16, None)
+    st = _lib.resnorm_fused_fwd(*p[:9], B, L, D, int(flags), _layout(gate_layout),
+                                _layout(ss_layout), float(eps), _stream(stream, dev))
+    if st != RN_OK:
+        raise RnError(st, last_error())
 
 
 def norm_scale_shift_fwd(y, x, weight, bias, scale, shift, B, L, D, flags,
                          ss_layout=(RN_BCAST, 0), eps=1e-6, stream=None) -> None:
     """Enqueue the norm-only op (C entry point of the same name); raises RnError."""
-    dev = _nss_checks(y, x, weight, bias, scale, shift, B, L, D, ss_layout, None)
-    _check(_lib.norm_scale_shift_fwd(_addr(y), _addr(x), _addr(weight), _addr(bias),
-                                     _addr(scale), _addr(shift), int(B), int(L), int(D),
-                                     int(flags), _layout(ss_layout), float(eps),
-                                     _stream(stream, dev)))
+    B, L, D = int(B), int(L), int(D)
+    dev, p = _nss_operands(y, x, weight, bias, scale, shift, B, L, D, ss_layout, RN_DTYPE_BF16,
+                           RN_DTYPE_BF16, None)
+    st = _lib.norm_scale_shift_fwd(*p[:6], B, L, D, int(flags), _layout(ss_layout), float(eps),
+                                   _stream(stream, dev))
+    if st != RN_OK:
+        raise RnError(st, last_error())
 
 
 def resnorm_fused_fwd_ex(y, residual_out, x, residual, gate, weight, bias, scale, shift, B, L,

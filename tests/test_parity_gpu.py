@@ -293,6 +293,34 @@ def test_empty_and_side_stream(rn, orc):
     compare_outputs(to_host(y), y_ref, what="side stream")
 
 
+def test_binding_refuses_device_tensors_it_cannot_pass(rn):
+    """The binding's checks on GPU tensors, before any library call: element
+    type, contiguity, one device for all operands; a refused call leaves the
+    outputs untouched."""
+    import torch
+    D, L = 512, 8
+    dev = torch.device("cuda:0")
+    x = torch.randn((L, D), device=dev).to(torch.bfloat16)
+    row = torch.zeros((1, D), dtype=torch.bfloat16, device=dev)
+    y = torch.full((L, D), 7.0, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(TypeError, match="y must be torch.bfloat16"):
+        rn.norm_scale_shift_fwd(y.to(torch.float16), x, None, None, row, row, 1, L, D, 0)
+    with pytest.raises(ValueError, match="x must be contiguous"):
+        rn.norm_scale_shift_fwd(y, torch.randn((D, L), device=dev).to(torch.bfloat16).t(), None,
+                                None, row, row, 1, L, D, 0)
+    with pytest.raises(ValueError, match="shift is on cpu but other operands are on cuda:0"):
+        rn.norm_scale_shift_fwd(y, x, None, None, row, row.cpu(), 1, L, D, 0)
+    with pytest.raises(TypeError, match="weight must be torch.float32"):
+        rn.norm_scale_shift_fwd_ex(y, x, row.view(-1), None, row, row, 1, L, D, rn.RN_WEIGHT,
+                                   affine_dtype=rn.RN_DTYPE_F32)
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+    # int addresses pass through to the library, which checks them itself
+    rn.norm_scale_shift_fwd(y.data_ptr(), x, None, None, row, row, 1, L, D, 0)
+    torch.cuda.synchronize()
+    assert not bool((y == 7.0).all())
+
+
 def test_repeated_calls_and_prepared_calls(rn, orc):
     """The library keeps each thread's last validated call with its launch
     plan, and rn.prepare checks a call once: alternating two problems (A, B,
