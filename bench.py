@@ -426,35 +426,75 @@ def launch_workload(rn, wl, d, y, ro, stream):
 
 
 REF_LIB = os.path.join(ROOT, "rmsnorm_diffusion_transformers_amd", "libtrafficref.so")
+# workloads with a traffic reference (libtrafficref.so: the kernel's memory
+# traffic at D 5120 without its arithmetic)
+REF_WORKLOADS = (HEADLINE, "nss_ln_b1_l176400_d5120")
+_ref_lib = []
+
+
+def _traffic_ref_lib():
+    import ctypes
+    if not _ref_lib:
+        if not os.path.exists(REF_LIB):
+            raise RuntimeError("libtrafficref.so is not built (expected at %s); build it with "
+                               "__graft_entry__.build()" % REF_LIB)
+        lib = ctypes.CDLL(REF_LIB)
+        P, I64 = ctypes.c_void_p, ctypes.c_int64
+        lib.rn_traffic_ref.argtypes = [P] * 7 + [I64] * 4 + [P]
+        lib.rn_traffic_ref.restype = ctypes.c_int
+        lib.rn_traffic_ref_nss.argtypes = [P] * 4 + [I64] * 3 + [P]
+        lib.rn_traffic_ref_nss.restype = ctypes.c_int
+        _ref_lib.append(lib)
+    return _ref_lib[0]
 
 
 def traffic_reference_call(wl, d, y, ro, stream):
-    """A launcher of the measurement reference (libtrafficref.so: the fused
-    op's memory traffic at D 5120 with per-frame gate/scale/shift, and none of
-    its arithmetic) on the workload's own tensors."""
-    import ctypes
-    if not os.path.exists(REF_LIB):
-        raise RuntimeError("libtrafficref.so is not built (expected at %s); build it with "
-                           "__graft_entry__.build()" % REF_LIB)
-    lib = ctypes.CDLL(REF_LIB)
-    P, I64 = ctypes.c_void_p, ctypes.c_int64
-    lib.rn_traffic_ref.argtypes = [P] * 7 + [I64] * 4 + [P]
-    lib.rn_traffic_ref.restype = ctypes.c_int
-    frames = wl.gate_layout[1]
-    assert wl.op == "fused" and wl.gate_layout == wl.ss_layout == (2, frames)
+    """A launcher of the measurement reference on the workload's own tensors:
+    for the fused op with per-frame gate/scale/shift, rn_traffic_ref; for the
+    norm-only op with broadcast scale/shift, rn_traffic_ref_nss (D 5120)."""
+    lib = _traffic_ref_lib()
     n = wl.B * wl.L * wl.D
-    for t, need in ((y, n), (ro, n), (d["x"], n), (d["residual"], n), (d["gate"], wl.B * frames * wl.D),
-                    (d["scale"], wl.B * frames * wl.D), (d["shift"], wl.B * frames * wl.D)):
+    if wl.op == "fused":
+        frames = wl.gate_layout[1]
+        assert wl.gate_layout == wl.ss_layout == (2, frames) and not wl.has_weight
+        m = wl.B * frames * wl.D
+        ops = ((y, n), (ro, n), (d["x"], n), (d["residual"], n), (d["gate"], m), (d["scale"], m),
+               (d["shift"], m))
+        fn = lib.rn_traffic_ref
+        tail = (wl.B, wl.L, wl.D, frames, stream.cuda_stream)
+    else:
+        assert wl.ss_layout == (0, 0) and not wl.has_weight
+        ops = ((y, n), (d["x"], n), (d["scale"], wl.D), (d["shift"], wl.D))
+        fn = lib.rn_traffic_ref_nss
+        tail = (wl.B, wl.L, wl.D, stream.cuda_stream)
+    for t, need in ops:
         assert t.is_cuda and t.is_contiguous() and t.element_size() == 2 and t.numel() >= need
-    args = (y.data_ptr(), ro.data_ptr(), d["x"].data_ptr(), d["residual"].data_ptr(),
-            d["gate"].data_ptr(), d["scale"].data_ptr(), d["shift"].data_ptr(),
-            wl.B, wl.L, wl.D, frames, stream.cuda_stream)
+    args = tuple(t.data_ptr() for t, _ in ops) + tail
 
     def call():
-        st = lib.rn_traffic_ref(*args)
+        st = fn(*args)
         if st != 0:
-            raise RuntimeError("rn_traffic_ref returned %d" % st)
+            raise RuntimeError("%s returned %d" % (fn.__name__, st))
     return call
+
+
+def traffic_reference_entry(wl, ref, ref_torch, gbs, torch_alloc, placement_kind):
+    """The bench line's record of a traffic reference: its rate on the
+    workload's placement and on torch's allocations, and the kernel's rate
+    over it on each."""
+    if wl.op == "fused":
+        what = ("rn_traffic_ref (libtrafficref.so): residual_out = x ^ residual, y = residual_out ^ "
+                "gate ^ scale ^ shift, the fused kernel's loads and stores")
+    else:
+        what = ("rn_traffic_ref_nss (libtrafficref.so): y = x ^ scale ^ shift, the norm-only "
+                "kernel's loads, stores and occupancy")
+    tr = {"kernel": what, "bytes_per_launch": wl.algorithmic_bytes(), "placement": placement_kind,
+          **(ref or {}), "torch_allocation": ref_torch}
+    if ref:
+        tr["kernel_over_reference"] = round(gbs / ref["GB/s"], 4)
+    if ref_torch and torch_alloc:
+        tr["kernel_over_reference_torch_allocation"] = round(torch_alloc["GB/s"] / ref_torch["GB/s"], 4)
+    return tr
 
 
 def traffic_reference_rate(wl, d, y, ro, steps, warmup):
@@ -934,7 +974,7 @@ def main():
     inp = make_inputs(wl)
     extra_out = [((wl.R, wl.D), torch.float32), ((wl.R, wl.D), torch.float8_e4m3fn)] if want_extras else []
     want_ref = not args.no_reference and args.workload == HEADLINE
-    ref_torch = ref_planned = None
+    ref_torch, ref_planned = {}, None
 
     # Row-kernel launches before the timed workloads (the torch-allocation
     # passes and the placement trials), so that a kernel trace can be split.
@@ -952,13 +992,13 @@ def main():
         # workload, measured first (each workload's tensors freed after it)
         for name, winp in [(wl.name, inp)] + list(comp_inputs.items()):
             w = synth.WORKLOADS[name]
-            if name == wl.name and want_ref:
+            if want_ref and name in REF_WORKLOADS:
                 dms, _, _, kept = time_workload(rn, w, args.steps, args.warmup, dev, keep=True,
                                                 inp=winp)
-                ref_torch = traffic_reference_rate(w, kept[0], kept[1], kept[2], args.steps,
-                                                   args.warmup)
-                log("traffic reference, torch allocations: %.4f ms/launch, %.1f GB/s"
-                    % (ref_torch["ms_per_launch"], ref_torch["GB/s"]))
+                ref_torch[name] = traffic_reference_rate(w, kept[0], kept[1], kept[2], args.steps,
+                                                         args.warmup)
+                log("%s traffic reference, torch allocations: %.4f ms/launch, %.1f GB/s"
+                    % (name, ref_torch[name]["ms_per_launch"], ref_torch[name]["GB/s"]))
                 del kept
                 torch.cuda.empty_cache()
             else:
@@ -1026,8 +1066,19 @@ def main():
         for name in COMPANIONS:
             wc = synth.WORKLOADS[name]
             cinp = comp_inputs.pop(name, None)
-            cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True, inp=cinp,
-                                           arena=arena, placement=plans.get(name))
+            cref = None
+            if want_ref and name in REF_WORKLOADS:
+                cms, _, cstats, ckept = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True,
+                                                      inp=cinp, arena=arena, placement=plans.get(name),
+                                                      keep=True)
+                cref = traffic_reference_rate(wc, ckept[0], ckept[1], ckept[2], args.steps, args.warmup)
+                log("%s traffic reference: %.4f ms/launch, %.1f GB/s" % (name, cref["ms_per_launch"],
+                                                                         cref["GB/s"]))
+                del ckept
+                torch.cuda.empty_cache()
+            else:
+                cms, _, cstats = time_workload(rn, wc, args.steps, args.warmup, dev, stats=True,
+                                               inp=cinp, arena=arena, placement=plans.get(name))
             del cinp
             cg = wc.algorithmic_bytes() / (cms * 1e-3) / 1e9
             log("%s: %.4f ms/launch, %.1f GB/s" % (wc.name, cms, cg))
@@ -1042,6 +1093,10 @@ def main():
                 entry["placement"] = plans[name].describe()
             if name in torch_alloc:
                 entry["torch_allocation"] = torch_alloc[name]
+            if cref is not None:
+                entry["traffic_reference"] = traffic_reference_entry(
+                    wc, cref, ref_torch.get(name), cg, torch_alloc.get(name),
+                    "planned" if name in plans else "default")
             companions.append(entry)
     if arena is not None:
         arena.release()
@@ -1083,18 +1138,8 @@ def main():
     if copy_placed is not None:
         line["copy_reference_placed"] = copy_placed
     if want_ref:
-        # the same bytes moved by a kernel with the fused kernel's memory
-        # instruction stream and no arithmetic, on the same tensors
-        tr = {"kernel": "rn_traffic_ref (libtrafficref.so): residual_out = x ^ residual, "
-                        "y = residual_out ^ gate ^ scale ^ shift, the fused kernel's loads and stores",
-              "bytes_per_launch": nbytes, "placement": placement["kind"],
-              **(ref_planned or {}), "torch_allocation": ref_torch}
-        if ref_planned:
-            tr["headline_over_reference"] = round(gbs / ref_planned["GB/s"], 4)
-        if ref_torch and wl.name in torch_alloc:
-            tr["headline_over_reference_torch_allocation"] = round(
-                torch_alloc[wl.name]["GB/s"] / ref_torch["GB/s"], 4)
-        line["traffic_reference"] = tr
+        line["traffic_reference"] = traffic_reference_entry(wl, ref_planned, ref_torch.get(wl.name), gbs,
+                                                            torch_alloc.get(wl.name), placement["kind"])
     if want_extras:
         line["variants"] = variants
         line["dit_forward_mix"] = mix

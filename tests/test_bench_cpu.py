@@ -89,3 +89,11 @@ def test_traffic_reference_library_refuses_what_it_does_not_take():
     assert f(*p, 1, 1 << 31, 5120, 1, None) == 1     # more than 2^31 - 1 rows
     assert f(*([None] * 7), 1, 16, 5120, 1, None) == 1
     assert f(*([None] * 7), 0, 16, 5120, 1, None) == 0   # empty: nothing launched
+    g = lib.rn_traffic_ref_nss
+    g.argtypes = [P] * 4 + [I64] * 3 + [P]
+    g.restype = ctypes.c_int
+    assert g(*p[:4], 1, 16, 2048, None) == 1
+    assert g(*p[:4], 1, 1 << 31, 5120, None) == 1
+    assert g(*p[:4], 1, -16, 5120, None) == 1
+    assert g(*([None] * 4), 1, 16, 5120, None) == 1
+    assert g(*([None] * 4), 1, 0, 5120, None) == 0
