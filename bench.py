@@ -788,6 +788,39 @@ def placement_counters(rn, dev, n=40):
     print(json.dumps({"workload": wl.name, "launches_each": n, "frac": res}), flush=True)
 
 
+def placement_arena_sizes(rn, dev, sizes=(3, 4, 5, 6, None), rounds=2):
+    """The headline's planned rate against the arena's size: for each number
+    of 32 GiB granules (None: all free HBM but 24 GiB), `rounds` fresh
+    arenas, each planned (rmsnorm_diffusion_transformers_amd.hbm) and timed
+    at its placement (40 launches after 10).  Prints one JSON line."""
+    import torch
+
+    import synth
+    from rmsnorm_diffusion_transformers_amd import hbm
+    wl = synth.WORKLOADS[HEADLINE]
+    inp = make_inputs(wl)
+    nb = wl.algorithmic_bytes()
+    ms, _, _ = time_workload(rn, wl, 40, 10, dev, inp=inp)
+    out = {"workload": wl.name, "torch_allocation_frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "arenas": []}
+    for rnd in range(rounds):
+        for g in sizes:
+            arena = hbm.HbmArena(dev, granules=g)
+            pl, info = plan_workload(rn, wl, inp, arena, dev)
+            ms, _, _ = time_workload(rn, wl, 40, 10, dev, inp=inp, arena=arena, placement=pl)
+            out["arenas"].append({"round": rnd, "granules": arena.granules, "gib": arena.nbytes >> 30,
+                                  "frac": round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "candidates": pl.candidates, "read_granule": pl.read_granule,
+                                  "write_granules": list(pl.write_granules),
+                                  "ms_first_pass_best": info["ms_first_pass_best"],
+                                  "ms_first_pass_worst": info["ms_first_pass_worst"]})
+            log("arena of %d granules: %.4f" % (arena.granules, out["arenas"][-1]["frac"]))
+            arena.release()
+            del arena
+            torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def placement_widths(rn, dev, widths=(2048, 3072, 4096, 5120, 6144, 8192, 10240)):
     """Fused LayerNorm (broadcast gate/scale/shift) and the norm-only op at
     several row widths, 176400 x 5120 elements each: torch's own allocations
@@ -930,6 +963,8 @@ def main():
     ap.add_argument("--placement-counters", action="store_true",
                     help="the headline kernel on three placements, 40 warm + 40 measured "
                          "launches each, for rocprofv3 counter runs")
+    ap.add_argument("--placement-arena-sizes", action="store_true",
+                    help="the headline's planned rate against the HBM arena's size")
     ap.add_argument("--placement-widths", action="store_true",
                     help="torch's allocations against a planned placement for the fused and "
                          "norm-only ops at several row widths")
@@ -960,6 +995,9 @@ def main():
         return
     if args.placement_widths:
         placement_widths(rn, dev)
+        return
+    if args.placement_arena_sizes:
+        placement_arena_sizes(rn, dev)
         return
     if args.placement_thirds:
         placement_thirds(rn, dev)
