@@ -22,12 +22,15 @@ So `plan` measures.  It packs the inputs into one 32 GiB granule of an
 arena, tries every assignment of the outputs to other granules (with two
 choices of the input granule), times the actual launch for each, times the
 three fastest again with more launches, and keeps the fastest of those:
-about 0.8 s for the headline workload (84 candidates).
+about 0.8 s for the headline workload in an arena of 8 granules (84
+candidates; 82.4 %), 0.1 s in one of 3 granules (96 GiB, 4 candidates;
+81.8 %).
 
 `HbmArena` owns one allocation that spans whole granules of the free
 device memory; callers take typed views of it at the offsets a `Placement`
 gives, and allocate their other tensors (weights, other activations) from
-the arena's heap, the part of every granule outside the placement slots.  The kernels themselves are unchanged; this module only decides where
+the arena's heap, the part of every granule outside the placement slots.
+The kernels themselves are unchanged; this module only decides where
 their operands live.  It uses torch for the device allocation and for event
 timing.
 """
