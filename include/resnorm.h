@@ -42,7 +42,8 @@
  * back-to-back allocations are) the fused op measured 75-79.5 % of 8 TB/s,
  * with the outputs in two different thirds 82-83 %.  Physical addresses are
  * not visible to the caller; the Python package's hbm module measures a good
- * placement inside one large allocation by timing these entry points.
+ * placement inside one large allocation (96 GiB is enough: 81.8 % for the
+ * fused op at B 1, L 176400, D 5120) by timing these entry points.
  */
 #ifndef RESNORM_H
 #define RESNORM_H
