@@ -210,17 +210,18 @@ def _stream(stream, device=None):
     return stream.cuda_stream
 
 
-_LAYOUTS = {}   # (kind, frames) -> rn_layout (passed by value; never modified)
+_LAYOUTS = {}   # (kind, frames) of plain ints -> rn_layout (passed by value; never modified)
 
 
 def _layout(lay) -> rn_layout:
     if isinstance(lay, rn_layout):
         return lay
-    c = _LAYOUTS.get(lay) if isinstance(lay, tuple) else None
+    plain = type(lay) is tuple and len(lay) == 2 and type(lay[0]) is int and type(lay[1]) is int
+    c = _LAYOUTS.get(lay) if plain else None
     if c is None:
         kind, frames = lay
         c = rn_layout(int(kind), int(frames))
-        if isinstance(lay, tuple) and len(_LAYOUTS) < 4096:
+        if plain and len(_LAYOUTS) < 4096:
             _LAYOUTS[lay] = c
     return c
 

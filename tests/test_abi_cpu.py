@@ -661,3 +661,16 @@ def test_norm_only_two_rows_per_workgroup(rn):
     assert rn.describe_launch(1, 2000, 5120, 0, False)["rows_per_block"] == 4
     assert rn.describe_launch(1, 176400, 5120, rn.RN_GATE, True)["rows_per_block"] == 4
     assert rn.describe_launch(1, 176400, 5120, rn.RN_WEIGHT, False)["rows_per_wave"] == 4
+
+
+def test_layout_structs_are_cached_only_for_plain_int_pairs(rn):
+    """The binding reuses one rn_layout per (kind, frames) pair of plain ints
+    (ctypes passes it by value); any other sequence is converted afresh."""
+    import numpy as np
+    a, b = rn._layout((rn.RN_FRAME, 49)), rn._layout((rn.RN_FRAME, 49))
+    assert a is b and (a.kind, a.frames) == (rn.RN_FRAME, 49)
+    c = rn._layout((np.int64(rn.RN_FRAME), 49))
+    assert c is not a and (c.kind, c.frames) == (rn.RN_FRAME, 49)
+    d = rn._layout([rn.RN_ROW, 0])
+    assert (d.kind, d.frames) == (rn.RN_ROW, 0)
+    assert rn._layout(a) is a
