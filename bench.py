@@ -1012,6 +1012,11 @@ def main():
     inp = make_inputs(wl)
     extra_out = [((wl.R, wl.D), torch.float32), ((wl.R, wl.D), torch.float8_e4m3fn)] if want_extras else []
     want_ref = not args.no_reference and args.workload == HEADLINE
+    ref_missing = want_ref and not os.path.exists(REF_LIB)
+    if ref_missing:
+        # a measurement aid, not the operation: the line says it is missing
+        log("libtrafficref.so is not built (%s); the traffic references are skipped" % REF_LIB)
+        want_ref = False
     ref_torch, ref_planned = {}, None
 
     # Row-kernel launches before the timed workloads (the torch-allocation
@@ -1175,6 +1180,8 @@ def main():
     }
     if copy_placed is not None:
         line["copy_reference_placed"] = copy_placed
+    if ref_missing:
+        line["traffic_reference"] = {"skipped": "libtrafficref.so is not built"}
     if want_ref:
         line["traffic_reference"] = traffic_reference_entry(wl, ref_planned, ref_torch.get(wl.name), gbs,
                                                             torch_alloc.get(wl.name), placement["kind"])
