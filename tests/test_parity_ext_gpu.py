@@ -293,10 +293,10 @@ def test_multi_row_shapes(rn, orc, case):
 
 
 def test_random_matrix(rn, orc):
-    """120 seeded random problems through the _ex entry points against the
+    """400 seeded random problems through the _ex entry points against the
     oracle, each at the bar of its output type; the planner picks whatever
     shape each problem gets (all four waves-per-row families are exercised)."""
-    cases = _random_cases(120, 4321)
+    cases = _random_cases(400, 4321)
     seen = set()
     for k, c in enumerate(cases):
         flags = (rn.RN_RMS if c["rms"] else 0) | (rn.RN_WEIGHT if c["aff"] else 0) | \
