@@ -70,7 +70,21 @@ def test_planned_placement_gives_the_same_bits():
     y_o, ro_o, _ = oracle.Oracle().fused(x, r, g, None, None, sc, sh, B, L, D, False,
                                          gate_layout=(2, F), ss_layout=(2, F), threads=8)
     compare_outputs(to_host(ya), y_o, to_host(oa), ro_o, what="placed")
-    del xa, ra, ya, oa, y32, ygroup
+    # the arena's heap hands out memory outside every placed tensor; writing
+    # it leaves the placed tensors as they were
+    placed = [(t.data_ptr(), t.data_ptr() + t.numel() * t.element_size()) for t in (xa, ra, ya, y32, oa)]
+    held = []
+    for shape, dt in (((D, D), bf), ((3, D), torch.float32), ((1 << 28,), torch.uint8)):
+        w = arena.alloc(shape, dt)
+        lo, hi = w.data_ptr(), w.data_ptr() + w.numel() * w.element_size()
+        assert (lo - base) % hbm.ALIGN == 0 and base <= lo and hi <= base + arena.nbytes
+        assert all(hi <= a or lo >= b for a, b in placed + held)
+        held.append((lo, hi))
+        w.view(torch.uint8).fill_(0xA5)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ya), y_ref) and np.array_equal(to_host(oa), ro_ref)
+    assert torch.equal(xa, xd) and torch.equal(ra, rd)
+    del xa, ra, ya, oa, y32, ygroup, w
     arena.release()
     torch.cuda.empty_cache()
 
