@@ -288,15 +288,17 @@ def time_workload(rn, wl, steps, warmup, dev, keep=False, stats=False, inp=None,
     return ms, wall, per_launch
 
 
-def extras(rn, dev_tensors, steps, warmup):
+def extras(rn, dev_tensors, steps, warmup, variants=True):
     """Variants of the op and the DiT-forward mix at the headline shape, on the
     headline's resident x / residual (B 1, L 176400, D 5120) and its outputs
-    (y, residual_out, and the binary32 and FP8 y placed beside y)."""
+    (y, residual_out, and the binary32 and FP8 y placed beside y; without
+    `variants`, only the mix, and those two are not needed)."""
     import numpy as np
     import torch
 
     import synth
-    d, y, ro, (y32, y8) = dev_tensors
+    d, y, ro, extra = dev_tensors
+    y32, y8 = extra if variants else (None, None)
     x, res = d["x"], d["residual"]
     R, D = x.shape
     dev = x.device
@@ -365,7 +367,7 @@ def extras(rn, dev_tensors, steps, warmup):
          nss_affine_bf16, 2 * act + 4 * row),
     ]
     out = []
-    for name, what, fn, nbytes in cases:
+    for name, what, fn, nbytes in (cases if variants else []):
         ms, _ = time_calls(fn, steps, warmup)
         gbs = nbytes / (ms * 1e-3) / 1e9
         log("%s: %.4f ms/launch, %.1f GB/s" % (name, ms, gbs))
@@ -382,7 +384,8 @@ def extras(rn, dev_tensors, steps, warmup):
             fused_bcast()
         nss_bcast()
 
-    fwd_ms, _ = time_calls(forward, 3, 1, settle_s=0)   # right after the variants: warm
+    # right after the variants, warm; on its own, after a settle phase
+    fwd_ms, _ = time_calls(forward, 3, 1, settle_s=0 if variants else SETTLE_S)
     log("DiT forward mix: %.2f ms per forward (121 calls)" % fwd_ms)
     mix = {"ms_per_forward": round(fwd_ms, 3),
            "calls": {"norm_scale_shift (no affine)": 41, "fused, fp32 affine": 40,
@@ -1018,6 +1021,7 @@ def main():
         log("libtrafficref.so is not built (%s); the traffic references are skipped" % REF_LIB)
         want_ref = False
     ref_torch, ref_planned = {}, None
+    mix_torch = None
 
     # Row-kernel launches before the timed workloads (the torch-allocation
     # passes and the placement trials), so that a kernel trace can be split.
@@ -1035,18 +1039,27 @@ def main():
         # workload, measured first (each workload's tensors freed after it)
         for name, winp in [(wl.name, inp)] + list(comp_inputs.items()):
             w = synth.WORKLOADS[name]
-            if want_ref and name in REF_WORKLOADS:
+            with_ref = want_ref and name in REF_WORKLOADS
+            with_mix = name == wl.name and want_extras
+            if with_ref or with_mix:
                 dms, _, _, kept = time_workload(rn, w, args.steps, args.warmup, dev, keep=True,
                                                 inp=winp)
+            else:
+                dms, _, _ = time_workload(rn, w, args.steps, args.warmup, dev, inp=winp)
+            prelude += settle_launches() + args.steps + args.warmup
+            if with_ref:
                 ref_torch[name] = traffic_reference_rate(w, kept[0], kept[1], kept[2], args.steps,
                                                          args.warmup)
                 log("%s traffic reference, torch allocations: %.4f ms/launch, %.1f GB/s"
                     % (name, ref_torch[name]["ms_per_launch"], ref_torch[name]["GB/s"]))
+            if with_mix:
+                # the mix on the same torch allocations (x, residual, y, residual_out)
+                _, mix_torch = extras(rn, kept, args.steps, args.warmup, variants=False)
+                prelude += 121 * (settle_launches() + 1 + 3)
+                log("DiT forward mix, torch allocations: %.2f ms" % mix_torch["ms_per_forward"])
+            if with_ref or with_mix:
                 del kept
                 torch.cuda.empty_cache()
-            else:
-                dms, _, _ = time_workload(rn, w, args.steps, args.warmup, dev, inp=winp)
-            prelude += settle_launches() + args.steps + args.warmup
             dg = w.algorithmic_bytes() / (dms * 1e-3) / 1e9
             log("%s, torch allocations: %.4f ms/launch, %.1f GB/s" % (name, dms, dg))
             torch_alloc[name] = {"ms_per_launch": round(dms, 5), "GB/s": round(dg, 1),
@@ -1187,6 +1200,8 @@ def main():
                                                             torch_alloc.get(wl.name), placement["kind"])
     if want_extras:
         line["variants"] = variants
+        if mix_torch is not None:
+            mix["torch_allocation_ms_per_forward"] = mix_torch["ms_per_forward"]
         line["dit_forward_mix"] = mix
         line["small_batch_latency"] = small_batch_latency(rn, dev)
     if not args.no_cpu_baseline:
