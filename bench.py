@@ -367,8 +367,10 @@ def extras(rn, dev_tensors, steps, warmup, variants=True):
          nss_affine_bf16, 2 * act + 4 * row),
     ]
     out = []
+    launches = 0   # row-kernel launches made here
     for name, what, fn, nbytes in (cases if variants else []):
         ms, _ = time_calls(fn, steps, warmup)
+        launches += settle_launches() + steps + warmup
         gbs = nbytes / (ms * 1e-3) / 1e9
         log("%s: %.4f ms/launch, %.1f GB/s" % (name, ms, gbs))
         out.append({"variant": name, "what": what, "ms_per_launch": round(ms, 5),
@@ -386,12 +388,14 @@ def extras(rn, dev_tensors, steps, warmup, variants=True):
 
     # right after the variants, warm; on its own, after a settle phase
     fwd_ms, _ = time_calls(forward, 3, 1, settle_s=0 if variants else SETTLE_S)
+    launches += 121 * ((0 if variants else settle_launches()) + 1 + 3)
     log("DiT forward mix: %.2f ms per forward (121 calls)" % fwd_ms)
     mix = {"ms_per_forward": round(fwd_ms, 3),
            "calls": {"norm_scale_shift (no affine)": 41, "fused, fp32 affine": 40,
                      "fused, no affine": 40},
            "shape": "B 1, L 176400, D 5120, broadcast (1,C) gate/scale/shift, LayerNorm",
-           "pages_prior_art_ms_per_forward_context": [171.6, 174.8]}
+           "pages_prior_art_ms_per_forward_context": [171.6, 174.8],
+           "row_kernel_launches": launches}
     del ys, bc, pb, w32, b32, w16, b16
     return out, mix
 
@@ -1021,7 +1025,7 @@ def main():
         log("libtrafficref.so is not built (%s); the traffic references are skipped" % REF_LIB)
         want_ref = False
     ref_torch, ref_planned = {}, None
-    mix_torch = None
+    mix_torch, variants_torch = None, []
 
     # Row-kernel launches before the timed workloads (the torch-allocation
     # passes and the placement trials), so that a kernel trace can be split.
@@ -1043,7 +1047,7 @@ def main():
             with_mix = name == wl.name and want_extras
             if with_ref or with_mix:
                 dms, _, _, kept = time_workload(rn, w, args.steps, args.warmup, dev, keep=True,
-                                                inp=winp)
+                                                inp=winp, extra_out=extra_out if with_mix else ())
             else:
                 dms, _, _ = time_workload(rn, w, args.steps, args.warmup, dev, inp=winp)
             prelude += settle_launches() + args.steps + args.warmup
@@ -1053,9 +1057,9 @@ def main():
                 log("%s traffic reference, torch allocations: %.4f ms/launch, %.1f GB/s"
                     % (name, ref_torch[name]["ms_per_launch"], ref_torch[name]["GB/s"]))
             if with_mix:
-                # the mix on the same torch allocations (x, residual, y, residual_out)
-                _, mix_torch = extras(rn, kept, args.steps, args.warmup, variants=False)
-                prelude += 121 * (settle_launches() + 1 + 3)
+                # the variants and the mix on the same torch allocations
+                variants_torch, mix_torch = extras(rn, kept, args.steps, args.warmup)
+                prelude += mix_torch["row_kernel_launches"]
                 log("DiT forward mix, torch allocations: %.2f ms" % mix_torch["ms_per_forward"])
             if with_ref or with_mix:
                 del kept
@@ -1202,6 +1206,11 @@ def main():
         line["variants"] = variants
         if mix_torch is not None:
             mix["torch_allocation_ms_per_forward"] = mix_torch["ms_per_forward"]
+        on_torch = {v["variant"]: v for v in variants_torch}
+        for v in variants:
+            t = on_torch.get(v["variant"])
+            if t is not None:
+                v["torch_allocation"] = {k: t[k] for k in ("ms_per_launch", "GB/s", "frac")}
         line["dit_forward_mix"] = mix
         line["small_batch_latency"] = small_batch_latency(rn, dev)
     if not args.no_cpu_baseline:
