@@ -1101,7 +1101,6 @@ def main():
     ms, wall, per_launch, kept = time_workload(rn, wl, args.steps, args.warmup, dev, keep=True,
                                                stats=True, inp=inp, arena=arena, placement=pl,
                                                extra_out=extra_out)
-    del inp
     gbs = nbytes / (ms * 1e-3) / 1e9
     log("%s: %.4f ms/launch, %.1f GB/s (%.1f%% of %g)" % (wl.name, ms, gbs, 100 * gbs / HBM_PEAK_GBS,
                                                           HBM_PEAK_GBS))
@@ -1113,6 +1112,7 @@ def main():
         copy_placed = {"kernel": "torch.neg bf16, x -> y at the planned offsets", "bytes_per_launch": nb,
                        "ms_per_launch": round(cms, 5), "GB/s": round(nb / cms / 1e6, 1),
                        "frac": round(nb / cms / 1e6 / HBM_PEAK_GBS, 4)}
+        del d, y   # views of the arena: the arena is released below
     if want_ref:
         ref_planned = traffic_reference_rate(wl, kept[0], kept[1], kept[2], args.steps, args.warmup)
         log("traffic reference: %.4f ms/launch, %.1f GB/s" % (ref_planned["ms_per_launch"],
@@ -1162,6 +1162,25 @@ def main():
         arena.release()
         arena = None
         torch.cuda.empty_cache()
+    if pl is not None:
+        # the same planning in an arena of 3 granules (96 GiB), the size a
+        # process holding a model's weights beside it can spare
+        try:
+            a3 = hbm.HbmArena(dev, granules=3)
+            pl3, info3 = plan_workload(rn, wl, inp, a3, dev)
+            ms3, _, _ = time_workload(rn, wl, args.steps, args.warmup, dev, inp=inp, arena=a3,
+                                      placement=pl3)
+            g3 = nbytes / (ms3 * 1e-3) / 1e9
+            placement["arena_3_granules"] = {
+                "gib": a3.nbytes >> 30, "candidates": pl3.candidates, "search_s": info3["search_s"],
+                "ms_per_launch": round(ms3, 5), "GB/s": round(g3, 1), "frac": round(g3 / HBM_PEAK_GBS, 4)}
+            log("%s in a 96 GiB arena: %.4f ms/launch, %.1f GB/s" % (wl.name, ms3, g3))
+            a3.release()
+            del a3
+        except (RuntimeError, ValueError) as e:
+            placement["arena_3_granules"] = {"note": str(e)}
+        torch.cuda.empty_cache()
+    del inp
     info = rn.describe_launch(wl.B, wl.L, wl.D, flags_of(rn, wl), wl.op == "fused",
                               wl.gate_layout or (0, 0), wl.ss_layout)
     ref = copy_reference(args.steps, args.warmup, dev)
