@@ -970,6 +970,8 @@ def main():
     ap.add_argument("--placement-counters", action="store_true",
                     help="the headline kernel on three placements, 40 warm + 40 measured "
                          "launches each, for rocprofv3 counter runs")
+    ap.add_argument("--small-batch", action="store_true",
+                    help="only the L = 16 latency measurements (small_batch_latency), one JSON line")
     ap.add_argument("--placement-arena-sizes", action="store_true",
                     help="the headline's planned rate against the HBM arena's size")
     ap.add_argument("--placement-widths", action="store_true",
@@ -1005,6 +1007,9 @@ def main():
         return
     if args.placement_arena_sizes:
         placement_arena_sizes(rn, dev)
+        return
+    if args.small_batch:
+        print(json.dumps({"small_batch_latency": small_batch_latency(rn, dev)}), flush=True)
         return
     if args.placement_thirds:
         placement_thirds(rn, dev)
