@@ -524,6 +524,68 @@ def test_degenerate_rows_ext_outputs(rn, orc):
         assert ok.all(), what + " FP8 codes more than one step away"
 
 
+def _near_constant_rows(D):
+    """Rows whose spread is a few bf16 ulps of their mean (|mean| / std up to
+    ~9000): all equal but one element one ulp up; a few elements one ulp up
+    or down; a large value with one element one ulp up."""
+    rows = []
+    r = np.full(D, 0x3F80, np.uint16)          # 1.0 ...
+    r[D // 3] = 0x3F81                         # ... and one 1.0078125
+    rows.append(r)
+    r = np.full(D, 0xC040, np.uint16)          # -3.0 ...
+    r[::97] = 0xC041                           # ... a few one ulp below
+    r[5::193] = 0xC03F                         # ... and a few one ulp above
+    rows.append(r)
+    r = np.full(D, 0x447A, np.uint16)          # 1000.0 ...
+    r[-1] = 0x447B                             # ... and one 1004.0
+    rows.append(r)
+    r = np.full(D, 0x3DCD, np.uint16)          # 0.1001 ...
+    r[:D // 2] = 0x3DCC                        # ... half of them one ulp lower
+    rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.0])
+@pytest.mark.parametrize("D", [5120, 1000])
+def test_near_constant_rows(rn, orc, D, eps):
+    """Rows whose values differ by a few bf16 ulps (|mean| >> std): the centred
+    values must not carry the binary32 rounding of the mean, which the
+    normalisation would magnify by |mean| / std; every output type at its
+    bar, both ops (the fused op with the row as residual and x = 0)."""
+    rows = _near_constant_rows(D)
+    L = rows.shape[0]
+    log("near-constant rows: D=%d eps=%g" % (D, eps))
+    sc = synth.random_bf16((1, D), 79, 6, a=0.0, b=0.1)
+    sh = synth.random_bf16((1, D), 79, 7, a=0.0, b=0.1)
+    zeros = np.zeros((L, D), np.uint16)
+    d = {k: to_dev(v) for k, v in (("h", rows), ("z", zeros), ("sc", sc), ("sh", sh))}
+    for fused in (False, True):
+        for y_dtype in (0, 1, 2):
+            what = "near-constant D=%d eps=%g fused=%s y=%d" % (D, eps, fused, y_dtype)
+            ydt = {0: torch.bfloat16, 1: torch.float32, 2: torch.float8_e4m3fn}[y_dtype]
+            y = torch.empty((L, D), dtype=ydt, device="cuda")
+            ys = torch.empty((L,), dtype=torch.float32, device="cuda") if y_dtype == 2 else None
+            if fused:
+                ro = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+                rn.resnorm_fused_fwd_ex(y, ro, d["z"], d["h"], None, None, None, d["sc"], d["sh"], 1, L,
+                                        D, 0, (BCAST, 0), (BCAST, 0), eps, y_dtype=y_dtype, y_scale=ys)
+                res = orc.fused(zeros, rows, None, None, None, sc, sh, 1, L, D, False, eps=eps,
+                                y_dtype=y_dtype)
+            else:
+                rn.norm_scale_shift_fwd_ex(y, d["h"], None, None, d["sc"], d["sh"], 1, L, D, 0,
+                                           (BCAST, 0), eps, y_dtype=y_dtype, y_scale=ys)
+                res = orc.nss(rows, None, None, sc, sh, 1, L, D, False, eps=eps, y_dtype=y_dtype)
+            torch.cuda.synchronize()
+            if fused:
+                assert np.array_equal(to_host(ro), rows), what
+            if y_dtype == 0:
+                compare_outputs(to_host(y), res[0], what=what)
+            elif y_dtype == 1:
+                check_y_f32(y.cpu().numpy(), res[0], what)
+            else:
+                check_y_fp8(y.view(torch.uint8).cpu().numpy(), ys.cpu().numpy(), res[0], res[-1], what)
+
+
 def test_maximum_row_count(rn, orc):
     """B * L = 2^31 - 1 rows (the largest the ABI accepts) at D = 8: 34 GB per
     tensor and a grid of 2^29 workgroups.  The inputs are a seeded block of
