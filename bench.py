@@ -1167,7 +1167,7 @@ def main():
         arena.release()
         arena = None
         torch.cuda.empty_cache()
-    if pl is not None:
+    if pl is not None and want_extras:
         # the same planning in an arena of 3 granules (96 GiB), the size a
         # process holding a model's weights beside it can spare
         try:
