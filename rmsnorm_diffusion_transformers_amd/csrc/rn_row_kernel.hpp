@@ -460,12 +460,15 @@ void row_kernel(const RowArgs a) {
     // ---- statistics (fp32) ----
     const float inv_d = 1.0f / (float)a.d;
     float mean = 0.f;
-    // LayerNorm: the rounding error of mean = total / D, as a second binary32
-    // term.  For a row whose values sit within a few bf16 ulps of each other
-    // (|mean| >> std) that error is comparable to the centred values, and the
-    // normalisation would magnify it by |mean| / std; the epilogue subtracts
-    // it (scaled by rstd) in the same fused multiply-add that applies rstd.
-    float mean_lo = 0.f;
+    // LayerNorm: mean * D - total, the rounding error of mean = total / D
+    // times D (exact in binary32: a multiple of ulp(mean) below D * ulp(mean)
+    // in magnitude).  For a row whose values sit within a few bf16 ulps of
+    // each other (|mean| >> std) the error is comparable to the centred
+    // values, and the normalisation would magnify it by |mean| / std; the
+    // epilogue adds it back, scaled by rstd / D, in the fused multiply-add
+    // that applies rstd.  (A row holding an infinity or a NaN gets NaN here,
+    // as it does everywhere.)
+    float mean_err = 0.f;
     float sq = 0.f;
     if constexpr (!OP::rms) {
       float sum = 0.f;
@@ -475,9 +478,7 @@ void row_kernel(const RowArgs a) {
         for (int j = 0; j < 4; ++j) sum += lo_f32(h[v][j]) + hi_f32(h[v][j]);
       const float total = row_reduce<W>(sum, Add{}, red_sum, wave, slot);
       mean = total / (float)a.d;
-      // total - mean * D is exact in binary32 (a multiple of ulp(mean) below
-      // D * ulp(mean) in magnitude), so only its division by D rounds
-      mean_lo = __builtin_isfinite(mean) ? __builtin_fmaf(-mean, (float)a.d, total) / (float)a.d : 0.f;
+      mean_err = __builtin_fmaf(mean, (float)a.d, -total);
       // Finite values summing beyond the binary32 range (|h| ~ 1e34 and more):
       // the mean again from h * 2^-k, k from the row's largest magnitude (a
       // power of two, exact for every element that stays inside the binary32
@@ -505,9 +506,7 @@ void row_kernel(const RowArgs a) {
         const float mean2 = total2 / (float)a.d;
         if (k != 0) {
           mean = __builtin_ldexpf(mean2, k);
-          mean_lo = __builtin_isfinite(mean2)
-                        ? __builtin_ldexpf(__builtin_fmaf(-mean2, (float)a.d, total2) / (float)a.d, k)
-                        : 0.f;
+          mean_err = __builtin_ldexpf(__builtin_fmaf(mean2, (float)a.d, -total2), k);
         }
       }
 #pragma unroll
@@ -577,7 +576,7 @@ void row_kernel(const RowArgs a) {
       var2 = var2 < 0.f ? 0.f : var2;
       if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
     }
-    [[maybe_unused]] const float nlo = -mean_lo * rstd;
+    [[maybe_unused]] const float nlo = mean_err * (inv_d * rstd);
 
     // weight / bias of vector v: from registers, or (staged in LDS) read into
     // wl / bl by read_lds(v) before the vector's outputs are computed
