@@ -546,15 +546,17 @@ def _near_constant_rows(D):
 
 
 @pytest.mark.parametrize("eps", [1e-6, 0.0])
-@pytest.mark.parametrize("D", [5120, 1000])
-def test_near_constant_rows(rn, orc, D, eps):
+@pytest.mark.parametrize("D,reps", [(5120, 1), (1000, 1), (5120, 1025)])
+def test_near_constant_rows(rn, orc, D, reps, eps):
     """Rows whose values differ by a few bf16 ulps (|mean| >> std): the centred
     values must not carry the binary32 rounding of the mean, which the
     normalisation would magnify by |mean| / std; every output type at its
-    bar, both ops (the fused op with the row as residual and x = 0)."""
-    rows = _near_constant_rows(D)
+    bar, both ops (the fused op with the row as residual and x = 0).  Four
+    rows reach the ten- and four-waves-per-row shapes; 4100 rows the one-wave
+    shapes (a partly filled last workgroup)."""
+    rows = np.tile(_near_constant_rows(D), (reps, 1))
     L = rows.shape[0]
-    log("near-constant rows: D=%d eps=%g" % (D, eps))
+    log("near-constant rows: D=%d L=%d eps=%g" % (D, L, eps))
     sc = synth.random_bf16((1, D), 79, 6, a=0.0, b=0.1)
     sh = synth.random_bf16((1, D), 79, 7, a=0.0, b=0.1)
     zeros = np.zeros((L, D), np.uint16)
