@@ -169,6 +169,31 @@ __device__ __forceinline__ bool overflowed(float total, const float* red) {
   return __builtin_amdgcn_readfirstlane((int)any) != 0;
 }
 
+// Whether a row's variance takes the rescaled recomputation, decided the
+// same way by every wave of the workgroup (as overflowed()): a binary32 sum
+// of squares that overflowed, or a variance below `floor` (2^-100 when eps
+// is below it, else -1: never), where the squares of tiny centred values
+// underflow binary32.  The variances are formed as the rows formed theirs
+// (partials in LDS order, times 1/D).
+template <int W, int RPB>
+__device__ __forceinline__ bool var_rescale(float var, const float* red, float inv_d, float floor) {
+  bool any;
+  if constexpr (W == 1 || RPB == 1) {
+    any = !__builtin_isfinite(var) || var < floor;
+  } else {
+    any = false;
+#pragma unroll
+    for (int q = 0; q < RPB; ++q) {
+      float t = red[q * W];
+#pragma unroll
+      for (int p = 1; p < W; ++p) t += red[q * W + p];
+      const float v = t * inv_d;
+      any = any || !__builtin_isfinite(v) || v < floor;
+    }
+  }
+  return __builtin_amdgcn_readfirstlane((int)any) != 0;
+}
+
 // Power of two s = 2^-k that brings a finite, nonzero magnitude m into
 // [1, 2); k = 0 (s = 1) when m is 0, infinite or NaN.
 __device__ __forceinline__ int scale_exp(float m) {
@@ -540,11 +565,17 @@ void row_kernel(const RowArgs a) {
     var = var < 0.f ? 0.f : var;
     float rstd = __builtin_amdgcn_rsqf(var + a.eps);
     // Finite centred values whose squares sum beyond the binary32 range
-    // (|h - mean| ~ 1e17-1e19 and more): the variance again from
-    // (h - mean) * 2^-k, k from the largest centred magnitude, and
-    // rstd = 2^-k / sqrt(var' + eps * 2^-2k).  Only rstd changes, so the
-    // epilogue is the same for every row.
-    if (overflowed<W, RPB>(var, red_sq)) {
+    // (|h - mean| ~ 1e17-1e19 and more), or, when eps is below 2^-100, so
+    // small that their squares underflow (|h - mean| below ~1e-19): the
+    // variance again from (h - mean) * 2^-k, k from the largest centred
+    // magnitude, and rstd = 2^-k / sqrt(var' + eps * 2^-2k) (kept as it was
+    // if eps * 2^-2k leaves the binary32 range: then eps alone decides
+    // rstd).  Only rstd changes, so the epilogue is the same for every row.
+    // Centred values in the binary32 subnormal range would need an rstd
+    // beyond it and stay as computed.
+    constexpr float kVarFloor = 0x1p-100f;
+    const float var_floor = a.eps < kVarFloor ? kVarFloor : -1.f;
+    if (var_rescale<W, RPB>(var, red_sq, inv_d, var_floor)) {
       float m = 0.f;
       const MaxNaN mx;
 #pragma unroll
@@ -557,16 +588,15 @@ void row_kernel(const RowArgs a) {
           m = mx(m, mx(d0, d1));
         }
       m = row_reduce<W>(m, mx, red_max, wave, slot);
-      const int k = __builtin_isfinite(var) ? 0 : scale_exp(m);
-      const float s = __builtin_ldexpf(1.0f, -k);
+      const int k = (__builtin_isfinite(var) && !(var < var_floor)) ? 0 : scale_exp(m);
       float sq2 = 0.f;
 #pragma unroll
       for (int v = 0; v < VPT; ++v) {
         float part_sq = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float d0 = (lo_f32(h[v][j]) - mean) * s;
-          const float d1 = (hi_f32(h[v][j]) - mean) * s;
+          const float d0 = __builtin_ldexpf(lo_f32(h[v][j]) - mean, -k);
+          const float d1 = __builtin_ldexpf(hi_f32(h[v][j]) - mean, -k);
           part_sq = __builtin_fmaf(d0, d0, part_sq);
           part_sq = __builtin_fmaf(d1, d1, part_sq);
         }
@@ -574,7 +604,8 @@ void row_kernel(const RowArgs a) {
       }
       float var2 = row_reduce<W>(sq2, Add{}, red_sq, wave, slot) * inv_d;
       var2 = var2 < 0.f ? 0.f : var2;
-      if (k != 0) rstd = s * __builtin_amdgcn_rsqf(__builtin_fmaf(a.eps * s, s, var2));
+      const float den = __builtin_ldexpf(a.eps, -2 * k) + var2;
+      if (k != 0 && __builtin_isfinite(den)) rstd = __builtin_ldexpf(__builtin_amdgcn_rsqf(den), -k);
     }
     [[maybe_unused]] const float nlo = mean_err * (inv_d * rstd);
 
