@@ -199,11 +199,21 @@ def _check_tensors(named):
     return _operands([(n, t, need, None) for n, t, need in named])[0]
 
 
+_RAW_STREAM = None     # torch's raw current-stream query, when it has one (else False)
+
+
 def _stream(stream, device=None):
     """The stream to enqueue on: the given one (a torch stream or a raw
-    handle), else torch's current stream of the operands' device."""
+    handle), else torch's current stream of the operands' device.  The
+    current stream is read through torch's raw-handle query where torch has
+    it (about 0.1 us against 1.1 us for building a torch Stream object)."""
+    global _RAW_STREAM
     if stream is None:
         torch = _torch_mod()
+        if _RAW_STREAM is None:
+            _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or False
+        if _RAW_STREAM:
+            return _RAW_STREAM(torch.cuda.current_device() if device is None else device)
         return torch.cuda.current_stream(device).cuda_stream
     if isinstance(stream, int):
         return stream

@@ -293,6 +293,28 @@ def test_empty_and_side_stream(rn, orc):
     compare_outputs(to_host(y), y_ref, what="side stream")
 
 
+def test_default_stream_is_torchs_current_stream(rn, orc):
+    """Without stream=, a call goes to torch's current stream of the operands'
+    device: the same handle torch reports, outside and inside a
+    torch.cuda.stream() context, and the call made there is ordered on it."""
+    import torch
+    assert rn._stream(None, 0) == torch.cuda.current_stream(0).cuda_stream
+    assert rn._stream(None) == torch.cuda.current_stream().cuda_stream
+    D = 512
+    inp = _small_problem(52, False, False, None, 0, (BCAST, 0), 1, 64, D)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert rn._stream(None, 0) == s.cuda_stream != torch.cuda.default_stream(0).cuda_stream
+        assert rn._stream(None) == s.cuda_stream
+        d = {k: to_dev(v) for k, v in inp.items()}
+        y = torch.empty_like(d["x"])
+        rn.norm_scale_shift_fwd(y, d["x"], None, None, d["scale"], d["shift"], 1, 64, D, 0,
+                                (BCAST, 0), 1e-6)
+    s.synchronize()
+    y_ref, _ = orc.nss(inp["x"], None, None, inp["scale"], inp["shift"], 1, 64, D, False)
+    compare_outputs(to_host(y), y_ref, what="current stream")
+
+
 def test_binding_refuses_device_tensors_it_cannot_pass(rn):
     """The binding's checks on GPU tensors, before any library call: element
     type, contiguity, one device for all operands; a refused call leaves the
