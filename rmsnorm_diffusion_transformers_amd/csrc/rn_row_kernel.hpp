@@ -50,8 +50,9 @@
 //     gfx950 permlane16/permlane32 swaps; with W > 1 the per-wave totals are
 //     combined through LDS in a fixed order.  Every lane and every wave of a
 //     row ends with the bit-identical total.  Rows of finite values whose
-//     binary32 sums overflow are recomputed on the row scaled by a power of
-//     two (a branch the common path only tests for).
+//     binary32 sums overflow, and (with eps below 2^-100) rows whose variance
+//     falls below 2^-100, are recomputed on the row scaled by a power of two
+//     (a branch the common path only tests for).
 //   * fp32 -> bf16 with v_cvt_pk_bf16_f32 (round to nearest even; fp32
 //     denormals are kept in these kernels).
 //   * Output y is bf16, binary32, or OCP FP8 E4M3 with a per-row scale
@@ -565,8 +566,9 @@ void row_kernel(const RowArgs a) {
     var = var < 0.f ? 0.f : var;
     float rstd = __builtin_amdgcn_rsqf(var + a.eps);
     // Finite centred values whose squares sum beyond the binary32 range
-    // (|h - mean| ~ 1e17-1e19 and more), or, when eps is below 2^-100, so
-    // small that their squares underflow (|h - mean| below ~1e-19): the
+    // (|h - mean| ~ 1e17-1e19 and more), or, when eps is below 2^-100, a
+    // variance below 2^-100 (centred values below ~1e-15, whose squares lose
+    // bits in the binary32 subnormal range or underflow to 0): the
     // variance again from (h - mean) * 2^-k, k from the largest centred
     // magnitude, and rstd = 2^-k / sqrt(var' + eps * 2^-2k) (kept as it was
     // if eps * 2^-2k leaves the binary32 range: then eps alone decides
