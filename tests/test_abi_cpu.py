@@ -674,3 +674,25 @@ def test_layout_structs_are_cached_only_for_plain_int_pairs(rn):
     d = rn._layout([rn.RN_ROW, 0])
     assert (d.kind, d.frames) == (rn.RN_ROW, 0)
     assert rn._layout(a) is a
+
+
+def test_stream_choice(rn, monkeypatch):
+    """An explicit stream wins (a raw handle as is, a torch stream by its
+    handle); without one the binding asks torch for the current stream of
+    the operands' device (the current device when no tensor was given),
+    through torch's raw-handle query or, where torch has none, a Stream
+    object."""
+    import types
+
+    import torch
+    assert rn._stream(1234) == 1234
+    assert rn._stream(types.SimpleNamespace(cuda_stream=77)) == 77
+    asked = []
+    monkeypatch.setattr(torch.cuda, "current_device", lambda: 3)
+    monkeypatch.setattr(rn, "_RAW_STREAM", lambda dev: asked.append(("raw", dev)) or 1000 + dev)
+    assert rn._stream(None, 1) == 1001 and rn._stream(None) == 1003
+    monkeypatch.setattr(rn, "_RAW_STREAM", False)
+    monkeypatch.setattr(torch.cuda, "current_stream",
+                        lambda dev=None: asked.append(("obj", dev)) or types.SimpleNamespace(cuda_stream=5))
+    assert rn._stream(None, 2) == 5
+    assert asked == [("raw", 1), ("raw", 3), ("obj", 2)]
