@@ -27,9 +27,12 @@
  *   - Frames are frame-major token blocks (49 latent frames x 3600 tokens =
  *     sequence 176400): sglang PR #36349, "Microbenchmark".
  *
- * Precision: the residual update is one binary32 sum rounded once to bf16
- * (the product of two bf16 values is exact in binary32, so fused and unfused
- * multiply-add agree).  Everything after it is binary64, with a two-pass
+ * Precision: the residual update is the exact residual + gate * x rounded
+ * once to binary32 (a fused multiply-add), then once to bf16.  The product of
+ * two bf16 values is exact in binary32 down to the normal range; below it a
+ * separately rounded product could round twice, or lose the sign of a
+ * product that underflows to zero, so the single rounding is written out
+ * with fmaf.  Everything after it is binary64, with a two-pass
  * (mean, then centred squares) variance with the biased 1/D estimator, and a
  * single correctly rounded conversion of the binary64 result to the output
  * type (bf16 by default; binary32; or FP8 E4M3 with a per-row scale).
@@ -138,12 +141,12 @@ void orc_f64_to_bf16_array(const double* in, uint16_t* out, int64_t n) {
 
 /* ---- the residual update ---------------------------------------------- */
 
-/* residual + gate * x in binary32, rounded once to bf16. */
+/* residual + gate * x: the exact value rounded once to binary32 (fmaf, or
+ * the plain sum without a gate), then once to bf16. */
 static uint16_t residual_update(uint16_t res, const uint16_t* gate_or_null, uint16_t x) {
   float r = bf16_to_f32(res);
   float xv = bf16_to_f32(x);
-  float branch = gate_or_null ? bf16_to_f32(*gate_or_null) * xv : xv;
-  float s = r + branch;
+  float s = gate_or_null ? fmaf(bf16_to_f32(*gate_or_null), xv, r) : r + xv;
   return orc_f64_to_bf16((double)s);
 }
 

@@ -468,8 +468,10 @@ void row_kernel(const RowArgs a) {
         for (int j = 0; j < 4; ++j) {
           float s0, s1;
           if constexpr (OP::gate) {
-            // gate * x is exact in binary32 (8-bit x 8-bit significands), so the
-            // fused multiply-add rounds exactly once, like residual + (gate * x).
+            // residual + gate * x rounded once: the fused multiply-add rounds
+            // the exact sum.  (gate * x alone is exact in binary32 unless it
+            // falls below the normal range, where rounding it first could also
+            // lose the sign of a product that underflows to zero.)
             s0 = __builtin_fmaf(lo_f32(gv[v][j]), lo_f32(xv[v][j]), lo_f32(h[v][j]));
             s1 = __builtin_fmaf(hi_f32(gv[v][j]), hi_f32(xv[v][j]), hi_f32(h[v][j]));
           } else {

@@ -160,6 +160,64 @@ def pin_residual_vs_torch(o, n_res: int = 64, n_gate: int = 16, seed: int = 2):
     assert np.array_equal(got1, got0)
 
 
+def _f32_nearest(q, zero_negative: bool) -> float:
+    """The binary32 value nearest the rational q, ties to the even
+    significand, with gradual underflow (quantum 2^-149 below 2^-126); a
+    result that rounds to zero keeps the sign of q, and q = 0 gives -0 only
+    when zero_negative."""
+    from fractions import Fraction
+    if q == 0:
+        return -0.0 if zero_negative else 0.0
+    a = abs(q)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    n = a / quantum
+    m = n.numerator // n.denominator
+    rem = n - m
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and m % 2 == 1):
+        m += 1
+    v = float(m * quantum)
+    return -v if q < 0 else v
+
+
+def pin_residual_one_rounding(o, n: int = 6000, seed: int = 11):
+    """Where gate * x falls below the binary32 normal range (bf16 subnormal or
+    tiny x, small gates, residuals of either sign near zero), residual_out is
+    the exact residual + gate * x rounded once to binary32 (exact rational
+    arithmetic, nearest-even with gradual underflow; an exact zero sum is -0
+    only when both the residual and the product are -0), then to bf16 by
+    torch's cast.  Includes products that underflow to zero below a +0
+    residual, where rounding the product first would return +0 instead of
+    the -0 of the exact sum."""
+    from fractions import Fraction
+    rng = np.random.default_rng(seed)
+    sign = lambda k: rng.integers(0, 2, k).astype(np.uint16) << 15  # noqa: E731
+    x = np.concatenate([rng.integers(1, 0x80, n).astype(np.uint16),             # bf16 subnormals
+                        rng.integers(0x0080, 0x0A00, n).astype(np.uint16)]) | sign(2 * n)
+    g = np.concatenate([rng.integers(0x2F00, 0x3F80, 2 * n).astype(np.uint16)]) | sign(2 * n)
+    r = np.concatenate([np.zeros(n // 2, np.uint16), rng.integers(1, 0x0300, 2 * n - n // 2).astype(np.uint16)])
+    r = r | sign(2 * n)
+    # the case that separates one rounding from two: -2^-133 * 2^-20 below +0
+    x = np.concatenate([x, _bits([-2.0 ** -133, 2.0 ** -133, -2.0 ** -130])])
+    g = np.concatenate([g, _bits([2.0 ** -20, -2.0 ** -20, 2.0 ** -30])])
+    r = np.concatenate([r, _bits([0.0, 0.0, 0.0])])
+    got = o.residual(r, g, x)
+    xf, gf, rf = (bf16_to_f32(v).astype(np.float64) for v in (x, g, r))
+    ref32 = np.empty(len(x), np.float32)
+    for i in range(len(x)):
+        prod = Fraction(gf[i]) * Fraction(xf[i])
+        prod_negative_zero = prod == 0 and (math.copysign(1.0, gf[i]) * math.copysign(1.0, xf[i]) < 0)
+        q = Fraction(rf[i]) + prod
+        ref32[i] = _f32_nearest(q, prod_negative_zero and math.copysign(1.0, rf[i]) < 0)
+    ref = torch.from_numpy(ref32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    bad = got != ref
+    assert not bad.any(), "x %04x gate %04x res %04x: oracle %04x exact %04x (%d cases)" % (
+        x[bad][0], g[bad][0], r[bad][0], got[bad][0], ref[bad][0], int(bad.sum()))
+    assert got[-3] == 0x8000 and got[-2] == 0x8000, (hex(got[-3]), hex(got[-2]))
+
+
 def pin_residual_gate_zero(o, seed: int = 3):
     """gate = 0 leaves the residual stream unchanged (finite x, no -0 residuals)."""
     rng = np.random.default_rng(seed)
@@ -616,6 +674,7 @@ def load_golden():
     from golden_cases import load_cases
     return load_cases()
 
-FAST_PINS = [pin_golden_worked_rows, pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero, pin_closed_forms, pin_modulation,
+FAST_PINS = [pin_golden_worked_rows, pin_affine_f32, pin_y_f32, pin_fp8_rows, pin_round_f64, pin_residual_gate_zero,
+             pin_residual_one_rounding, pin_closed_forms, pin_modulation,
              pin_torch_norms, pin_layouts, pin_fused_is_nss_of_residual, pin_scale_invariance,
              pin_random_rows_ld, pin_invariants]

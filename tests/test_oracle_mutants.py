@@ -14,10 +14,13 @@ import oracle
 import pins
 
 MUTANTS = {
-    "gate_dropped": ("float branch = gate_or_null ? bf16_to_f32(*gate_or_null) * xv : xv;",
-                     "float branch = xv;"),
-    "gate_scales_residual": ("float s = r + branch;",
-                             "float s = (gate_or_null ? bf16_to_f32(*gate_or_null) * r : r) + xv;"),
+    "gate_dropped": ("float s = gate_or_null ? fmaf(bf16_to_f32(*gate_or_null), xv, r) : r + xv;",
+                     "float s = r + xv;"),
+    "gate_scales_residual": ("float s = gate_or_null ? fmaf(bf16_to_f32(*gate_or_null), xv, r) : r + xv;",
+                             "float s = gate_or_null ? fmaf(bf16_to_f32(*gate_or_null), r, xv) : r + xv;"),
+    "residual_product_rounded_first": (
+        "float s = gate_or_null ? fmaf(bf16_to_f32(*gate_or_null), xv, r) : r + xv;",
+        "float s = gate_or_null ? r + bf16_to_f32(*gate_or_null) * xv : r + xv;"),
     "norm_of_x_not_residual": ("h[c] = orc_bf16_to_f64(ro);",
                                "h[c] = orc_bf16_to_f64(x[k]);"),
     "modulation_sign": ("n * (1.0 + orc_bf16_to_f64(scale_row[c]))",

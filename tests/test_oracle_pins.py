@@ -21,6 +21,10 @@ def test_residual_gate_zero_is_identity(orc):
     pins.pin_residual_gate_zero(orc)
 
 
+def test_residual_one_rounding_below_the_normal_range(orc):
+    pins.pin_residual_one_rounding(orc)
+
+
 def test_closed_forms(orc):
     pins.pin_closed_forms(orc)
 

@@ -190,6 +190,40 @@ def test_residual_every_bf16_x(rn, orc):
         X[bad][0], Rr[bad][0], G[bad][0], got[bad][0], ref[bad][0])
 
 
+def test_residual_products_below_the_normal_range(rn, orc):
+    """residual_out for every bf16 x against residuals of either sign at and
+    near zero and gates down to 2^-33, where gate * x falls below the binary32
+    normal range or underflows: bit-exact with the oracle's one rounding of
+    the exact sum, including the -0 of a product that underflows below a +0
+    residual."""
+    import torch
+    xs = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    res_vals = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x0040, 0x807F, 0x0080, 0x8080,
+                         0x0100, 0x3F80], np.uint16)
+    gates = np.array([0x3580, 0xB580, 0x2F00, 0xAF00, 0x3A80, 0x37C0, 0x3F80, 0x0001], np.uint16)
+    D = 1024
+    X = np.tile(xs, len(res_vals) * len(gates)).reshape(-1, D)
+    Rr = np.repeat(np.repeat(res_vals, len(xs)), len(gates)).reshape(-1, D)
+    G = np.tile(np.repeat(gates, len(xs)), len(res_vals)).reshape(-1, D)
+    R = X.shape[0]
+    log("residual below the normal range: %d rows of %d" % (R, D))
+    zeros = np.zeros((1, D), np.uint16)
+    dx, dr, dg, dz = to_dev(X), to_dev(Rr), to_dev(G), to_dev(zeros)
+    y = torch.empty_like(dx)
+    ro = torch.empty_like(dx)
+    rn.resnorm_fused_fwd(y, ro, dx, dr, dg, None, None, dz, dz, 1, R, D, rn.RN_GATE,
+                         (ROW, 0), (BCAST, 0), 1e-6)
+    torch.cuda.synchronize()
+    got = to_host(ro)
+    ref = orc.residual(Rr, G, X)
+    gnan = (got & 0x7FFF) > 0x7F80
+    rnan = (ref & 0x7FFF) > 0x7F80
+    bad = (gnan != rnan) | (~gnan & (got != ref))
+    assert not bad.any(), "x %04x res %04x gate %04x: gpu %04x oracle %04x (%d)" % (
+        X[bad][0], Rr[bad][0], G[bad][0], got[bad][0], ref[bad][0], int(bad.sum()))
+    assert ((Rr == 0x0000) & (ref == 0x8000)).any()     # the underflowed -0 case occurs
+
+
 def test_determinism_permutation_and_norm_of_residual(rn, orc):
     """Reruns are bitwise identical; permuting rows permutes the outputs bit-
     exactly (broadcast layouts); the fused y equals the norm-only op applied to
