@@ -107,7 +107,10 @@ typedef struct {
  * For every activation row r and column c (sglang PR #36349, "Microbenchmark":
  * flydsl_fused_residual_norm_scale_shift(residual, x, gate, weight, bias,
  * scale, shift, norm_type, eps); the formula is this library's reading of it):
- *   s                   = f32(residual[r,c]) + f32(gate[g(r),c]) * f32(x[r,c])   (binary32)
+ *   s                   = f32(residual[r,c]) + f32(gate[g(r),c]) * f32(x[r,c])
+ *                         (the exact value rounded once to binary32, as a fused
+ *                         multiply-add rounds it; also when gate * x falls below
+ *                         the binary32 normal range)
  *   residual_out[r,c]   = bf16_rne(s)
  *   h                   = residual_out[r, :] as f32
  *   LayerNorm:  n = (h - mean(h)) * rsqrt(var(h) + eps)    (biased variance, 1/D)
